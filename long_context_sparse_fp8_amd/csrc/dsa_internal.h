@@ -1,0 +1,58 @@
+// dsa_internal.h -- launchers behind the C ABI (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Calls with at most this many queries use the split-key indexer (decode
+// shape); larger calls use the query-blocked one (prefill shape).
+constexpr int kIndexerDecodeMaxQ = 256;
+
+struct IndexerArgs {
+    const uint8_t *q_fp8;
+    const float *q_scale;
+    const float *w;
+    int64_t w_ld;
+    const uint8_t *key_cache;
+    const float *key_scale;
+    int64_t n_pages;
+    const int32_t *page_table;
+    int64_t pt_ld;
+    const int32_t *q_seq;
+    const int32_t *q_pos;
+    int32_t n_q, h_i, d_i;
+    float *scores;
+    int64_t scores_ld;
+};
+
+struct MlaArgs {
+    const uint16_t *q;
+    const void *kv_cache;
+    const float *kv_scale;
+    bool fp8;
+    int64_t n_slots;
+    const int32_t *kv_slot_table;
+    int64_t kv_pt_ld;
+    const int32_t *q_seq;
+    const int32_t *idx;
+    int32_t n_q, h, k;
+    float sm_scale;
+    uint16_t *out;
+    float *lse;
+};
+
+hipError_t launch_indexer_store(const uint8_t *k, const float *ks, const int64_t *slot, int32_t n, int32_t d_i,
+                                uint8_t *cache, float *scache, int64_t n_pages, hipStream_t stream);
+hipError_t launch_kv_store(const uint16_t *kv, const int64_t *slot, int32_t n, int dt, void *cache, float *scale,
+                           int64_t n_slots, hipStream_t stream);
+hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream);
+hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k, int32_t *idx,
+                       hipStream_t stream);
+hipError_t launch_mla_prefill(const MlaArgs &a, hipStream_t stream);
+hipError_t launch_mla_decode(const MlaArgs &a, int n_splits, void *ws, hipStream_t stream);
+int mla_decode_auto_splits(int32_t n_q, int32_t k);
+size_t mla_decode_ws_bytes(int32_t n_q, int32_t h, int32_t n_splits);
+
+}  // namespace dsa

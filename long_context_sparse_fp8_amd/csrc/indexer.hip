@@ -1,0 +1,314 @@
+// indexer.hip -- Lightning Indexer scores on FP8 MFMA (gfx950).
+//
+// score[t, s] = q_scale[t] * k_scale[s] * sum_j w[t, j] * ReLU(sum_i q[t, j, i] k[s, i])
+// for s in [0, q_pos[t]] (DeepSeek-V3.2-Exp deployment article, section 1:
+// an FP8 scorer over predecessor tokens; context-parallel article, section
+// 1: relevance is a reduce-sum over the indexer heads).  Keys come from the
+// page-64 key & key_scale cache (SGLang DeepSeek-V3.2 announcement).
+//
+// MFMA mapping (v_mfma_f32_32x32x64_f8f6f4): A = 32 indexer heads of one
+// query, B = 32 keys, K = 64 bytes of the head dim.  Lane group g = l / 32
+// owns head-dim bytes [g * D_I/2, (g+1) * D_I/2) in both operands (the same
+// K permutation on both sides leaves the dot product unchanged).  The fp32
+// accumulator gives lane l one key (l % 32) and 16 heads, so ReLU, weight
+// and most of the head sum stay in the lane; one half-wave swap finishes the
+// head sum and leaves key l of the 64-key page in lane l for a coalesced
+// store.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+template <int H_I, int D_I>
+struct IdxShape {
+    static constexpr int HT = (H_I + 31) / 32;   // 32-head MFMA row tiles
+    static constexpr int KC = D_I / 64;          // 32-byte K chunks per lane
+    static constexpr int HALF = D_I / 2;         // head-dim bytes owned by a lane group
+    static constexpr int ROW = D_I + 16;         // padded LDS row (bytes): conflict-free 16-byte reads
+    static constexpr int CH = D_I / 16;          // 16-byte chunks per key
+};
+
+// Register-resident operands of one query.
+template <int H_I, int D_I>
+struct QueryFrag {
+    using S = IdxShape<H_I, D_I>;
+    i32x8 a[S::HT][S::KC];
+    float w[S::HT][16];
+};
+
+template <int H_I, int D_I>
+__device__ __forceinline__ void load_query(QueryFrag<H_I, D_I> &q, const uint8_t *__restrict__ q_fp8,
+                                           const float *__restrict__ w, int64_t w_ld, int t, int lane) {
+    using S = IdxShape<H_I, D_I>;
+    const int g = lane >> 5;
+#pragma unroll
+    for (int ht = 0; ht < S::HT; ++ht) {
+        const int head = 32 * ht + (lane & 31);
+#pragma unroll
+        for (int c = 0; c < S::KC; ++c) {
+            i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (head < H_I) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(q_fp8 + ((int64_t)t * H_I + head) * D_I +
+                                                                   g * S::HALF + 32 * c);
+                const uint4 lo = src[0], hi = src[1];
+                v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+            q.a[ht][c] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int hh = 32 * ht + 8 * (i >> 2) + 4 * g + (i & 3);
+            q.w[ht][i] = hh < H_I ? w[(int64_t)t * w_ld + hh] : 0.0f;
+        }
+    }
+}
+
+// One query against one 64-key page whose B fragments are in `b`.
+// Returns the (unscaled) score of key `lane` of the page.
+template <int H_I, int D_I>
+__device__ __forceinline__ float page_scores(const QueryFrag<H_I, D_I> &q,
+                                             const i32x8 (&b)[2][IdxShape<H_I, D_I>::KC]) {
+    using S = IdxShape<H_I, D_I>;
+    float part[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        f32x16 acc[S::HT];
+#pragma unroll
+        for (int ht = 0; ht < S::HT; ++ht) {
+            acc[ht] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < S::KC; ++c) acc[ht] = mfma_f8_32x32x64(q.a[ht][c], b[kt][c], acc[ht]);
+        }
+        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < S::HT; ++ht) {
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) {
+                s0 = fmaf(q.w[ht][i + 0], fmaxf(acc[ht][i + 0], 0.0f), s0);
+                s1 = fmaf(q.w[ht][i + 1], fmaxf(acc[ht][i + 1], 0.0f), s1);
+                s2 = fmaf(q.w[ht][i + 2], fmaxf(acc[ht][i + 2], 0.0f), s2);
+                s3 = fmaf(q.w[ht][i + 3], fmaxf(acc[ht][i + 3], 0.0f), s3);
+            }
+        }
+        part[kt] = (s0 + s1) + (s2 + s3);
+    }
+    // lane i < 32: key i (tile 0); lane 32 + i: key 32 + i (tile 1)
+    return halves_reduce_scatter(part[0], part[1]);
+}
+
+// ------------------------------------------------------------------ prefill
+// Workgroup = 4 waves = 4 * QPW consecutive queries.  Queries of the same
+// sequence share every key page, staged once in LDS (double-buffered).
+template <int H_I, int D_I, int QPW>
+__global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
+    const uint8_t *__restrict__ q_fp8, const float *__restrict__ q_scale, const float *__restrict__ w, int64_t w_ld,
+    const uint8_t *__restrict__ key_cache, const float *__restrict__ key_scale, int64_t n_pages,
+    const int32_t *__restrict__ page_table, int64_t pt_ld, const int32_t *__restrict__ q_seq,
+    const int32_t *__restrict__ q_pos, int32_t n_q, float *__restrict__ scores, int64_t ld) {
+    using S = IdxShape<H_I, D_I>;
+    constexpr int QB = 4 * QPW;
+    constexpr int kChunks = kPage * S::CH;             // 16-byte chunks per page
+    constexpr int kPer = (kChunks + 255) / 256;        // per thread
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kPage * S::ROW];
+    __shared__ float sbuf[2][kPage];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+    const int nqb = (n_q + QB - 1) / QB;
+    const int t0 = (nqb - 1 - (int)blockIdx.x) * QB;   // latest (longest) query blocks first
+
+    QueryFrag<H_I, D_I> q[QPW];
+    float qs[QPW];
+    int qp[QPW];
+#pragma unroll
+    for (int qq = 0; qq < QPW; ++qq) {
+        const int t = t0 + wave * QPW + qq;
+        const int tc = t < n_q ? t : n_q - 1;
+        load_query<H_I, D_I>(q[qq], q_fp8, w, w_ld, tc, lane);
+        qs[qq] = q_scale[tc];
+        qp[qq] = q_pos[tc];
+    }
+    const int64_t max_page = (ld + kPage - 1) / kPage;
+
+    uint32_t done = 0;
+#pragma unroll
+    for (int r = 0; r < QB; ++r)
+        if (t0 + r >= n_q) done |= 1u << r;
+
+    while (done != (1u << QB) - 1) {
+        // next sequence group among the not-yet-processed rows (uniform over the workgroup)
+        const int first = __builtin_ctz(~done);
+        const int seq = q_seq[t0 + first];
+        uint32_t active = 0;
+        int pmax = -1;
+#pragma unroll
+        for (int r = 0; r < QB; ++r) {
+            if (!((done >> r) & 1u) && q_seq[t0 + r] == seq) {
+                active |= 1u << r;
+                pmax = max(pmax, q_pos[t0 + r]);
+            }
+        }
+        done |= active;
+        int64_t n_pg = pmax < 0 ? 0 : (int64_t)pmax / kPage + 1;
+        if (n_pg > max_page) n_pg = max_page;
+        const int32_t *pt_row = page_table + (int64_t)seq * pt_ld;
+
+        uint4 stage[kPer];
+        float sstage = 0.0f;
+        auto fetch = [&](int64_t p) {
+            const int64_t phys = p < pt_ld ? (int64_t)pt_row[p] : -1;
+            const bool ok = phys >= 0 && phys < n_pages;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int ch = threadIdx.x + 256 * j;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (ok && ch < kChunks)
+                    v = reinterpret_cast<const uint4 *>(key_cache + phys * (kPage * D_I))[ch];
+                stage[j] = v;
+            }
+            if (threadIdx.x < kPage) sstage = ok ? key_scale[phys * kPage + threadIdx.x] : __builtin_nanf("");
+        };
+        auto commit = [&](int buf) {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int ch = threadIdx.x + 256 * j;
+                if (ch < kChunks) {
+                    const int key = ch / S::CH, col = ch % S::CH;
+                    *reinterpret_cast<uint4 *>(&kbuf[buf][key * S::ROW + col * 16]) = stage[j];
+                }
+            }
+            if (threadIdx.x < kPage) sbuf[buf][threadIdx.x] = sstage;
+        };
+
+        if (n_pg > 0) {
+            fetch(0);
+            commit(0);
+        }
+        __syncthreads();
+        for (int64_t p = 0; p < n_pg; ++p) {
+            const int buf = (int)(p & 1);
+            if (p + 1 < n_pg) fetch(p + 1);
+            i32x8 b[2][S::KC];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const uint8_t *row = &kbuf[buf][(32 * kt + (lane & 31)) * S::ROW + g * S::HALF];
+#pragma unroll
+                for (int c = 0; c < S::KC; ++c) {
+                    const uint4 lo = *reinterpret_cast<const uint4 *>(row + 32 * c);
+                    const uint4 hi = *reinterpret_cast<const uint4 *>(row + 32 * c + 16);
+                    b[kt][c] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                }
+            }
+            const float ksc = sbuf[buf][lane];
+            const int64_t key = p * kPage + lane;
+#pragma unroll
+            for (int qq = 0; qq < QPW; ++qq) {
+                const int r = wave * QPW + qq;
+                if ((active >> r) & 1u) {
+                    const float sc = page_scores<H_I, D_I>(q[qq], b);
+                    if (key <= qp[qq] && key < ld)
+                        scores[(int64_t)(t0 + r) * ld + key] = sc * (qs[qq] * ksc);
+                }
+            }
+            if (p + 1 < n_pg) commit(buf ^ 1);
+            __syncthreads();
+        }
+    }
+}
+
+// ------------------------------------------------------------------ decode
+// Workgroup = one query x a range of key pages; the 4 waves take pages
+// round-robin and load B fragments straight from the cache (each key byte is
+// used by exactly one query, so there is nothing to share through LDS).
+template <int H_I, int D_I>
+__global__ __launch_bounds__(256) void indexer_decode_kernel(
+    const uint8_t *__restrict__ q_fp8, const float *__restrict__ q_scale, const float *__restrict__ w, int64_t w_ld,
+    const uint8_t *__restrict__ key_cache, const float *__restrict__ key_scale, int64_t n_pages,
+    const int32_t *__restrict__ page_table, int64_t pt_ld, const int32_t *__restrict__ q_seq,
+    const int32_t *__restrict__ q_pos, int32_t n_q, float *__restrict__ scores, int64_t ld, int pages_per_split) {
+    using S = IdxShape<H_I, D_I>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+    const int t = blockIdx.x;
+    const int pos = q_pos[t];
+    int64_t n_pg = pos < 0 ? 0 : (int64_t)pos / kPage + 1;
+    const int64_t max_page = (ld + kPage - 1) / kPage;
+    if (n_pg > max_page) n_pg = max_page;
+    const int64_t p_begin = (int64_t)blockIdx.y * pages_per_split;
+    const int64_t p_end = min(n_pg, p_begin + pages_per_split);
+    if (p_begin >= p_end) return;
+
+    QueryFrag<H_I, D_I> q;
+    load_query<H_I, D_I>(q, q_fp8, w, w_ld, t, lane);
+    const float qs = q_scale[t];
+    const int32_t *pt_row = page_table + (int64_t)q_seq[t] * pt_ld;
+
+    auto fetch = [&](int64_t p, i32x8 (&b)[2][S::KC], float &ksc) {
+        const int64_t phys = p < pt_ld ? (int64_t)pt_row[p] : -1;
+        const bool ok = phys >= 0 && phys < n_pages;
+        const uint8_t *base = key_cache + (ok ? phys : 0) * (kPage * D_I);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int c = 0; c < S::KC; ++c) {
+                i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (ok) {
+                    const uint4 *src = reinterpret_cast<const uint4 *>(base + (32 * kt + (lane & 31)) * D_I +
+                                                                       g * S::HALF + 32 * c);
+                    const uint4 lo = src[0], hi = src[1];
+                    v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                }
+                b[kt][c] = v;
+            }
+        }
+        ksc = ok ? key_scale[phys * kPage + lane] : __builtin_nanf("");
+    };
+
+    i32x8 b[2][S::KC];
+    float ksc;
+    int64_t p = p_begin + wave;
+    if (p < p_end) fetch(p, b, ksc);
+    while (p < p_end) {
+        i32x8 bn[2][S::KC];
+        float kn = 0.0f;
+        const int64_t pn = p + 4;
+        if (pn < p_end) fetch(pn, bn, kn);
+        const float sc = page_scores<H_I, D_I>(q, b);
+        const int64_t key = p * kPage + lane;
+        if (key <= pos && key < ld) scores[(int64_t)t * ld + key] = sc * (qs * ksc);
+        p = pn;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int c = 0; c < S::KC; ++c) b[kt][c] = bn[kt][c];
+        ksc = kn;
+    }
+}
+
+// ------------------------------------------------------------------ launch
+template <int H_I, int D_I>
+static hipError_t launch_indexer_t(const IndexerArgs &a, hipStream_t stream) {
+    if (a.n_q <= kIndexerDecodeMaxQ) {
+        // few queries: split each query's key range over workgroups
+        const int pps = 64;
+        const int64_t splits = (a.pt_ld + pps - 1) / pps;
+        dim3 grid((unsigned)a.n_q, (unsigned)(splits > 0 ? splits : 1));
+        hipLaunchKernelGGL((indexer_decode_kernel<H_I, D_I>), grid, dim3(256), 0, stream, a.q_fp8, a.q_scale, a.w,
+                           a.w_ld, a.key_cache, a.key_scale, a.n_pages, a.page_table, a.pt_ld, a.q_seq, a.q_pos,
+                           a.n_q, a.scores, a.scores_ld, pps);
+    } else {
+        constexpr int QPW = 2;
+        const int nqb = (a.n_q + 4 * QPW - 1) / (4 * QPW);
+        hipLaunchKernelGGL((indexer_prefill_kernel<H_I, D_I, QPW>), dim3((unsigned)nqb), dim3(256), 0, stream,
+                           a.q_fp8, a.q_scale, a.w, a.w_ld, a.key_cache, a.key_scale, a.n_pages, a.page_table, a.pt_ld,
+                           a.q_seq, a.q_pos, a.n_q, a.scores, a.scores_ld);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream) {
+    if (a.h_i == 64 && a.d_i == 128) return launch_indexer_t<64, 128>(a, stream);
+    if (a.h_i == 16 && a.d_i == 64) return launch_indexer_t<16, 64>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

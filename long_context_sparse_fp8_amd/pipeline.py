@@ -1,0 +1,87 @@
+"""One pass of the DSA hot path, as a sequence of C-ABI calls.
+
+prefill_step: cache stores -> indexer scores -> top-k -> sparse MLA (prefill)
+decode_step:  cache stores -> indexer scores -> top-k -> sparse MLA (decode)
+
+The caller owns every buffer (`PrefillState` / `DecodeState` hold them so a
+timed loop allocates nothing); each stage is one call into libdsa.so on the
+current stream.
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+@dataclass
+class PrefillState:
+    key_cache: torch.Tensor        # [n_pages, 64, d_i] uint8
+    key_scale: torch.Tensor        # [n_pages, 64] f32
+    kv_cache: torch.Tensor         # [n_slots, 576] bf16, or uint8 for an FP8 cache
+    kv_scale: Optional[torch.Tensor]
+    scores: torch.Tensor           # [rows, ld] f32
+    idx: torch.Tensor              # [rows, k] int32
+    out: torch.Tensor              # [rows, H, 512] bf16
+    lse: Optional[torch.Tensor]    # [rows, H] f32
+
+
+def alloc_prefill(n_pages, d_i, n_slots, rows, ld, k, h, kv_fp8=False, with_lse=True, device="cuda"):
+    kv_cache = torch.zeros((n_slots, B.DK), dtype=torch.uint8 if kv_fp8 else torch.bfloat16, device=device)
+    return PrefillState(
+        key_cache=torch.zeros((n_pages, B.PAGE, d_i), dtype=torch.uint8, device=device),
+        key_scale=torch.zeros((n_pages, B.PAGE), dtype=torch.float32, device=device),
+        kv_cache=kv_cache,
+        kv_scale=torch.zeros(n_slots, dtype=torch.float32, device=device) if kv_fp8 else None,
+        scores=torch.empty((rows, ld), dtype=torch.float32, device=device),
+        idx=torch.empty((rows, k), dtype=torch.int32, device=device),
+        out=torch.empty((rows, h, B.DV), dtype=torch.bfloat16, device=device),
+        lse=torch.empty((rows, h), dtype=torch.float32, device=device) if with_lse else None,
+    )
+
+
+def store_tokens(st: PrefillState, ik, ik_scale, ik_slot, kv, kv_slot):
+    """Write new tokens' indexer keys and latent rows into the two caches."""
+    B.indexer_cache_store(ik, ik_scale, ik_slot, st.key_cache, st.key_scale)
+    B.kv_cache_store(kv, kv_slot, st.kv_cache, st.kv_scale)
+
+
+def prefill_step(st: PrefillState, iq, iq_scale, w, page_table, kv_slot_table, q_seq, q_pos, q, k, sm_scale,
+                 row0=0, rows=None):
+    """Indexer -> top-k -> sparse MLA for query rows [row0, row0 + rows) of the given
+    query tensors (the caches must already hold every key those rows can see)."""
+    n = iq.shape[0] if rows is None else rows
+    sc = st.scores[:n]
+    ix = st.idx[:n]
+    B.indexer_scores(iq, iq_scale, w, st.key_cache, st.key_scale, page_table, q_seq, q_pos, sc)
+    B.topk(sc, q_pos, k, ix)
+    B.sparse_mla_prefill(q, st.kv_cache, kv_slot_table, q_seq, ix, sm_scale, st.out[:n],
+                         st.lse[:n] if st.lse is not None else None, kv_scale=st.kv_scale)
+
+
+@dataclass
+class DecodeState:
+    scores: torch.Tensor           # [B, ld] f32
+    idx: torch.Tensor              # [B, k] int32
+    out: torch.Tensor              # [B, H, 512] bf16
+    lse: torch.Tensor              # [B, H] f32
+    ws: torch.Tensor               # decode workspace (uint8)
+    n_splits: int
+
+
+def alloc_decode(batch, ld, k, h, n_splits=0, device="cuda"):
+    need = B.sparse_mla_decode_workspace_size(batch, h, k, n_splits)
+    return DecodeState(scores=torch.empty((batch, ld), dtype=torch.float32, device=device),
+                       idx=torch.empty((batch, k), dtype=torch.int32, device=device),
+                       out=torch.empty((batch, h, B.DV), dtype=torch.bfloat16, device=device),
+                       lse=torch.empty((batch, h), dtype=torch.float32, device=device),
+                       ws=torch.empty(max(need, 1), dtype=torch.uint8, device=device), n_splits=n_splits)
+
+
+def decode_step(ds: DecodeState, caches: PrefillState, iq, iq_scale, w, page_table, kv_slot_table, q_seq, q_pos, q,
+                k, sm_scale):
+    B.indexer_scores(iq, iq_scale, w, caches.key_cache, caches.key_scale, page_table, q_seq, q_pos, ds.scores)
+    B.topk(ds.scores, q_pos, k, ds.idx)
+    B.sparse_mla_decode(q, caches.kv_cache, kv_slot_table, q_seq, ds.idx, sm_scale, ds.out, ds.lse,
+                        kv_scale=caches.kv_scale, n_splits=ds.n_splits, ws=ds.ws)

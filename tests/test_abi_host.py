@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/dsa.h declares, and rejects bad arguments on the
+host before anything is enqueued (each error path is forced from the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import long_context_sparse_fp8_amd as dsa
+    return dsa.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["dsa_indexer_cache_store", "dsa_kv_cache_store", "dsa_indexer_scores", "dsa_topk",
+              "dsa_sparse_mla_prefill", "dsa_sparse_mla_decode", "dsa_topk_workspace_size",
+              "dsa_sparse_mla_decode_workspace_size", "dsa_abi_version", "dsa_status_string", "dsa_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert L.dsa_abi_version() == 1
+
+
+def test_status_strings(L):
+    assert L.dsa_status_string(0) == b"DSA_OK"
+    assert L.dsa_status_string(3) == b"DSA_ERR_UNSUPPORTED"
+    assert L.dsa_status_string(99) == b"DSA_ERR_UNKNOWN"
+
+
+P = ctypes.c_void_p
+A = P(0x1000)          # aligned non-null dummy pointer (never dereferenced: validation fails first)
+MIS = P(0x1004)        # misaligned
+
+
+def _err(L):
+    return L.dsa_last_error().decode()
+
+
+def test_indexer_scores_validation(L):
+    # unsupported (h_i, d_i)
+    rc = L.dsa_indexer_scores(A, A, A, 32, A, A, 10, A, 4, A, A, 5, 32, 128, A, 100, None)
+    assert rc == 3 and "h_i" in _err(L)
+    # null pointer
+    rc = L.dsa_indexer_scores(None, A, A, 64, A, A, 10, A, 4, A, A, 5, 64, 128, A, 100, None)
+    assert rc == 1 and "q_fp8" in _err(L)
+    # misaligned
+    rc = L.dsa_indexer_scores(A, A, A, 64, A, A, 10, A, 4, A, A, 5, 64, 128, MIS, 100, None)
+    assert rc == 4 and "scores" in _err(L)
+    # bad leading dimensions / counts
+    assert L.dsa_indexer_scores(A, A, A, 7, A, A, 10, A, 4, A, A, 5, 64, 128, A, 100, None) == 2
+    assert L.dsa_indexer_scores(A, A, A, 64, A, A, 10, A, 0, A, A, 5, 64, 128, A, 100, None) == 2
+    assert L.dsa_indexer_scores(A, A, A, 64, A, A, 10, A, 4, A, A, -1, 64, 128, A, 100, None) == 2
+    # n_q == 0 is a no-op, even with NULL pointers
+    assert L.dsa_indexer_scores(None, None, None, 64, None, None, 10, None, 4, None, None, 0, 64, 128,
+                                None, 100, None) == 0
+
+
+def test_topk_validation(L):
+    assert L.dsa_topk(A, 100, A, 4, 0, A, None, 0, None) == 3
+    assert L.dsa_topk(A, 100, A, 4, 2049, A, None, 0, None) == 3
+    assert L.dsa_topk(A, 0, A, 4, 16, A, None, 0, None) == 2
+    assert L.dsa_topk(None, 100, A, 4, 16, A, None, 0, None) == 1
+    assert L.dsa_topk(A, 100, A, 4, 16, MIS, None, 0, None) == 4
+    assert L.dsa_topk_workspace_size(4, 100, 16) == 0
+
+
+def test_mla_validation(L):
+    f = ctypes.c_float(1 / 24)
+    args = lambda **kw: [kw.get("q", A), A, kw.get("kvs", A), kw.get("dt", 0), kw.get("n_slots", 100), A,
+                         kw.get("ld", 100), A, A, kw.get("n_q", 4), kw.get("h", 128), kw.get("k", 2048),
+                         kw.get("sm", f), A, kw.get("lse", None)]
+    assert L.dsa_sparse_mla_prefill(*args(h=24), None) == 3
+    assert L.dsa_sparse_mla_prefill(*args(h=144), None) == 3
+    assert L.dsa_sparse_mla_prefill(*args(k=0), None) == 3
+    assert L.dsa_sparse_mla_prefill(*args(k=4096), None) == 3
+    assert L.dsa_sparse_mla_prefill(*args(dt=5), None) == 3
+    assert L.dsa_sparse_mla_prefill(*args(n_slots=0), None) == 2
+    assert L.dsa_sparse_mla_prefill(*args(sm=ctypes.c_float(0.0)), None) == 2
+    assert L.dsa_sparse_mla_prefill(*args(q=None), None) == 1
+    assert L.dsa_sparse_mla_prefill(*args(dt=1, kvs=None), None) == 1
+    assert L.dsa_sparse_mla_prefill(*args(lse=MIS), None) == 4
+    need = L.dsa_sparse_mla_decode_workspace_size(64, 128, 2048, 0)
+    assert need > 0
+    assert L.dsa_sparse_mla_decode(*args(n_q=64), 0, A, need - 1, None) == 5
+    assert L.dsa_sparse_mla_decode(*args(n_q=64), 33, A, need, None) == 3
+    assert L.dsa_sparse_mla_decode(*args(n_q=64), 0, None, need, None) == 1
+    assert L.dsa_sparse_mla_decode_workspace_size(64, 128, 2048, 4) == 64 * 4 * 128 * 512 * 4 + \
+        ((64 * 4 * 128 * 4 + 255) // 256) * 256 + 256
+
+
+def test_cache_store_validation(L):
+    assert L.dsa_indexer_cache_store(A, A, A, 10, 96, A, A, 4, None) == 3
+    assert L.dsa_indexer_cache_store(A, A, A, -1, 128, A, A, 4, None) == 2
+    assert L.dsa_indexer_cache_store(None, A, A, 10, 128, A, A, 4, None) == 1
+    assert L.dsa_indexer_cache_store(None, None, None, 0, 128, None, None, 4, None) == 0
+    assert L.dsa_kv_cache_store(A, A, 10, 2, A, A, 100, None) == 3
+    assert L.dsa_kv_cache_store(A, A, 10, 1, A, None, 100, None) == 1
+    assert L.dsa_kv_cache_store(A, MIS, 10, 0, A, None, 100, None) == 4

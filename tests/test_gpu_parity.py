@@ -1,0 +1,376 @@
+"""GPU parity of the HIP path (called through the C ABI) against the CPU oracle,
+at sizes the oracle finishes in seconds: the tiny prefill (L=1024, 16x64
+indexer, 8 MLA heads, k=256) in full, the 64x128 / 128-head shapes on
+shortened sequences, ragged tails and the edge cases of the method.
+
+Index parity follows three levels (the GPU's FP8 MFMA sums in an order and
+precision of its own, so its fp32 scores can differ from the exact oracle in
+the last bits):
+  1. top-k from identical scores is bit-exact, always;
+  2. in the exact-arithmetic regime E1 every evaluation order gives the same
+     bits, so scores and the indexer -> top-k indices are bit-exact end to end;
+  3. on N(0, 1) inputs every GPU score is within an a-priori bound of the
+     exact score (and the 5e-2 FP8 tolerance).
+Sparse-MLA outputs are compared with the oracle evaluated on the GPU's own
+indices: max-abs relative error <= 2e-2 (bf16 KV) and 5e-2 (FP8 KV).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.configs import CONFIGS, SM_SCALE, Config
+from gpu_common import (DEV, say, bits16, u8, max_abs_rel, indexer_abs_scale, setup_prefill, run_prefill,
+                        oracle_threads)
+import long_context_sparse_fp8_amd as dsa
+from long_context_sparse_fp8_amd import pipeline as P
+
+pytestmark = pytest.mark.gpu
+
+BOUND_C = 2.0 ** -9      # |gpu - exact| <= BOUND_C * sum of |terms| (measured MFMA error ~2^-13)
+TOL_BF16, TOL_FP8 = 2e-2, 5e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    dsa.lib()
+
+
+def _cfg(base, **kw):
+    d = dict(CONFIGS[base].__dict__)
+    d.update(kw)
+    return Config(**d)
+
+
+# ------------------------------------------------------------------ cache stores
+@pytest.mark.parametrize("cfg", ["C1", "C3"])
+def test_cache_store_bytes(cfg):
+    say(f"[cache_store] {cfg}")
+    c = _cfg(cfg, L=2048) if cfg == "C3" else CONFIGS[cfg]
+    inp = synth.make_prefill(c, L=c.L, materialize_q=False)
+    st = setup_prefill(inp, c.k)
+    torch.cuda.synchronize()
+    slots = inp.ik_slot.numpy()
+    kc = u8(st.key_cache).reshape(-1, c.d_i)
+    np.testing.assert_array_equal(kc[slots], u8(inp.ik))
+    np.testing.assert_array_equal(st.key_scale.cpu().numpy().reshape(-1)[slots], inp.ik_scale.numpy())
+    kvs = inp.kv_slot_table[0].numpy()
+    np.testing.assert_array_equal(bits16(st.kv_cache)[kvs], bits16(inp.kv))
+
+
+def test_cache_store_fp8_matches_oracle_quantizer():
+    say("[cache_store] fp8 kv")
+    n, n_slots = 777, 1000
+    kv = synth.bf16_normal((n, 576), 901)
+    kv[3] = 0.0                                          # all-zero row -> scale 1
+    kv[5, :7] = torch.tensor([1e-8, -3e-7, 2.0 ** -133, 5e4, -5e4, 0.0, 1.0], dtype=torch.bfloat16)
+    slot = synth.randperm(n_slots, 902)[:n].long()
+    slot[10] = -1                                        # skipped
+    cache = torch.zeros((n_slots, 576), dtype=torch.uint8, device=DEV)
+    scale = torch.full((n_slots,), -1.0, dtype=torch.float32, device=DEV)
+    dsa.kv_cache_store(kv.to(DEV), slot.to(DEV), cache, scale)
+    torch.cuda.synchronize()
+    codes, scales = oracle.kv_quantize(bits16(kv))
+    s = slot.numpy()
+    ok = s >= 0
+    np.testing.assert_array_equal(u8(cache)[s[ok]], codes[ok])
+    np.testing.assert_array_equal(scale.cpu().numpy()[s[ok]], scales[ok])
+    assert scale.cpu().numpy()[np.setdiff1d(np.arange(n_slots), s[ok])].max() == -1.0
+
+
+# ------------------------------------------------------------------ indexer
+def _oracle_scores(inp, rows, ld):
+    return oracle.indexer_scores(u8(inp.iq[rows]), inp.iq_scale[rows].numpy(), inp.w[rows].numpy(), u8(inp.ik),
+                                 inp.ik_scale.numpy(), inp.q_pos[rows].numpy(), ld=ld, n_threads=oracle_threads())
+
+
+@pytest.mark.parametrize("base,L,paged", [("C1", 1024, False), ("C1", 1000, True), ("C2", 2048, False),
+                                          ("C3", 2560, True), ("C2", 200, True)])
+def test_indexer_exact_regime_bitexact(base, L, paged):
+    """E1: integer FP8 codes, power-of-two scales, weights in (1/16)Z: the GPU
+    scores equal the oracle's bit for bit, and so do the selected indices."""
+    say(f"[indexer E1] {base} L={L} paged={paged}")
+    c = _cfg(base, paged=paged)
+    inp = synth.make_prefill(c, exact=True, L=L)
+    st = run_prefill(inp, c.k)
+    g = st.scores.cpu().numpy()
+    rows = np.arange(L)
+    ref = _oracle_scores(inp, rows, L)
+    mask = np.arange(L)[None, :] <= inp.q_pos.numpy()[:, None]
+    assert np.array_equal(g[mask], ref[mask]), f"{(g[mask] != ref[mask]).sum()} score mismatches"
+    ridx = oracle.topk(ref, inp.q_pos.numpy(), c.k, n_threads=oracle_threads())
+    np.testing.assert_array_equal(st.idx.cpu().numpy(), ridx)
+
+
+@pytest.mark.parametrize("base,L,paged", [("C1", 1024, False), ("C2", 1536, True), ("C2", 777, False)])
+def test_indexer_normal_within_bound(base, L, paged):
+    say(f"[indexer N(0,1)] {base} L={L} paged={paged}")
+    c = _cfg(base, paged=paged)
+    inp = synth.make_prefill(c, L=L)
+    st = run_prefill(inp, c.k)
+    g = st.scores.cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, L, max(1, L // 97)), np.arange(max(0, L - 9), L)]))
+    ref = _oracle_scores(inp, rows, L)
+    A = indexer_abs_scale(inp.iq, inp.iq_scale, inp.w, inp.ik, inp.ik_scale, rows)
+    mask = np.arange(L)[None, :] <= inp.q_pos.numpy()[rows][:, None]
+    err = np.abs(g[rows] - ref)[mask]
+    bound = BOUND_C * A[mask] + 1e-30
+    ratio = float((err / bound).max())
+    say(f"  max |gpu-exact| / (2^-9 * sum|terms|) = {ratio:.4f}; max-abs-rel = {max_abs_rel(g[rows][mask], ref[mask]):.2e}")
+    assert ratio <= 1.0
+    assert max_abs_rel(g[rows][mask], ref[mask]) <= TOL_FP8
+
+
+def test_indexer_shared_weights_and_columns_untouched():
+    say("[indexer] shared weights, untouched columns")
+    c = CONFIGS["C1"]
+    inp = synth.make_prefill(c, L=300)
+    st = setup_prefill(inp, c.k, ld=320)
+    st.scores.fill_(12345.0)
+    w0 = inp.w[0].contiguous()
+    dsa.indexer_scores(inp.iq.to(DEV), inp.iq_scale.to(DEV), w0.to(DEV), st.key_cache, st.key_scale,
+                       inp.page_table.to(DEV), inp.q_seq.to(DEV), inp.q_pos.to(DEV), st.scores[:300], w_shared=True)
+    torch.cuda.synchronize()
+    g = st.scores[:300].cpu().numpy()
+    ref = oracle.indexer_scores(u8(inp.iq), inp.iq_scale.numpy(), w0.numpy(), u8(inp.ik), inp.ik_scale.numpy(),
+                                inp.q_pos.numpy(), ld=320, w_shared=True)
+    mask = np.arange(320)[None, :] <= inp.q_pos.numpy()[:, None]
+    A = indexer_abs_scale(inp.iq, inp.iq_scale, w0.expand(300, -1), inp.ik, inp.ik_scale, np.arange(300))
+    A = np.concatenate([A, np.zeros((300, 20))], axis=1)
+    assert (np.abs(g - ref)[mask] <= BOUND_C * A[mask] + 1e-30).all()
+    assert (g[~mask] == 12345.0).all()
+
+
+# ------------------------------------------------------------------ top-k
+@pytest.mark.parametrize("case", ["normal", "ties", "zeros", "short_rows", "wide"])
+def test_topk_bitexact_from_identical_scores(case):
+    say(f"[topk] {case}")
+    rng = np.random.default_rng(sum(map(ord, case)))
+    n_q, ld, k = 300, 5000, 2048
+    if case == "wide":
+        n_q, ld, k = 40, 131072, 2048
+    s = rng.standard_normal((n_q, ld)).astype(np.float32)
+    if case == "ties":
+        s = np.round(s * 2) / 2
+    if case == "zeros":
+        s[:, ::2] = 0.0
+        s[:, 1::4] = -0.0
+    pos = rng.integers(0, ld, size=n_q).astype(np.int32)
+    pos[:4] = [0, k - 1, k, ld - 1]
+    if case == "short_rows":
+        pos = rng.integers(0, 2 * k, size=n_q).astype(np.int32)
+    if case == "ties":
+        k = 333
+    sd = torch.from_numpy(s).to(DEV)
+    pd = torch.from_numpy(pos).to(DEV)
+    idx = torch.full((n_q, k), -7, dtype=torch.int32, device=DEV)
+    dsa.topk(sd, pd, k, idx)
+    torch.cuda.synchronize()
+    ref = oracle.topk(s, pos, k, n_threads=oracle_threads())
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+
+
+def test_topk_k_one_and_all_equal():
+    say("[topk] k=1 / all equal")
+    s = np.zeros((3, 100), np.float32)
+    s[1, 37] = 1.0
+    s[2] = -np.arange(100, dtype=np.float32)
+    pos = np.int32([99, 99, 50])
+    for k in (1, 7):
+        idx = torch.empty((3, k), dtype=torch.int32, device=DEV)
+        dsa.topk(torch.from_numpy(s).to(DEV), torch.from_numpy(pos).to(DEV), k, idx)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(s, pos, k))
+
+
+# ------------------------------------------------------------------ sparse MLA
+def _mla_ref(inp, idx, rows, kv_fp8=False, st=None):
+    q = inp.q if inp.q is not None else inp.q_chunk(0, inp.iq.shape[0])
+    if kv_fp8:
+        codes, scales = oracle.kv_quantize(bits16(inp.kv))
+        return oracle.sparse_mla(bits16(q[rows]), codes, idx[rows], SM_SCALE, kv_scale=scales,
+                                 n_threads=oracle_threads())
+    return oracle.sparse_mla(bits16(q[rows]), bits16(inp.kv), idx[rows], SM_SCALE, n_threads=oracle_threads())
+
+
+@pytest.mark.parametrize("base,L,paged,kv_fp8", [("C1", 1024, False, False), ("C1", 1024, True, True),
+                                                 ("C2", 2304, True, False), ("C2", 2304, False, True),
+                                                 ("C2", 333, False, False)])
+def test_sparse_mla_prefill_vs_oracle(base, L, paged, kv_fp8):
+    say(f"[mla prefill] {base} L={L} paged={paged} fp8={kv_fp8}")
+    c = _cfg(base, paged=paged)
+    inp = synth.make_prefill(c, L=L)
+    st = run_prefill(inp, c.k, kv_fp8=kv_fp8)
+    idx = st.idx.cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, L, max(1, L // 40)), [L - 1], np.arange(min(L, c.k) - 2, min(L, c.k) + 2)]))
+    rows = rows[(rows >= 0) & (rows < L)]
+    ref_o, ref_l = _mla_ref(inp, idx, rows, kv_fp8)
+    g_o = st.out[rows].float().cpu().numpy()
+    g_l = st.lse[rows].cpu().numpy()
+    e = max_abs_rel(g_o, ref_o)
+    el = float(np.abs(g_l - ref_l).max())
+    say(f"  out max-abs-rel = {e:.3e}, lse max abs err = {el:.3e}")
+    assert e <= (TOL_FP8 if kv_fp8 else TOL_BF16)
+    assert el <= 2e-2
+
+
+def test_dense_degeneration_k_covers_all():
+    """k >= L: every predecessor is selected and the output is dense causal MLA."""
+    say("[dense degeneration] C1, k = L")
+    c = CONFIGS["C1"]
+    L = 512
+    inp = synth.make_prefill(c, L=L)
+    st = run_prefill(inp, L)
+    idx = st.idx.cpu().numpy()
+    exp = np.where(np.arange(L)[None, :] <= np.arange(L)[:, None], np.arange(L)[None, :], -1)
+    np.testing.assert_array_equal(idx, exp)
+    ref_o, ref_l = oracle.dense_mla(bits16(inp.q), bits16(inp.kv), inp.q_pos.numpy(), SM_SCALE,
+                                    n_threads=oracle_threads())
+    assert max_abs_rel(st.out.float().cpu().numpy(), ref_o) <= TOL_BF16
+
+
+def test_single_index_gives_value_row():
+    say("[mla] single index")
+    c = CONFIGS["C2"]
+    n, N = 16, 500
+    q = synth.bf16_normal((n, c.h, 576), 911).to(DEV)
+    kv = synth.bf16_normal((N, 576), 912)
+    kv_cache = kv.to(DEV)
+    table = torch.arange(N, dtype=torch.int32, device=DEV).reshape(1, N)
+    idx = torch.full((n, 64), -1, dtype=torch.int32)
+    sel = torch.randint(0, N, (n,), generator=synth.gen(913))
+    idx[:, 0] = sel
+    idx[3, :] = -1
+    idx[3, 40] = int(sel[3])                             # a lone index in the middle of the list
+    out = torch.empty((n, c.h, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((n, c.h), dtype=torch.float32, device=DEV)
+    dsa.sparse_mla_prefill(q, kv_cache, table, torch.zeros(n, dtype=torch.int32, device=DEV), idx.to(DEV),
+                           SM_SCALE, out, lse)
+    torch.cuda.synchronize()
+    got = bits16(out).reshape(n, c.h, 512)
+    for t in range(n):
+        np.testing.assert_array_equal(got[t], np.broadcast_to(bits16(kv[sel[t]])[:512], (c.h, 512)))
+
+
+def test_empty_selection_and_out_of_range_entries():
+    say("[mla] empty / out-of-range entries")
+    n, N, h = 4, 100, 16
+    q = synth.bf16_normal((n, h, 576), 921).to(DEV)
+    kv = synth.bf16_normal((N, 576), 922)
+    table = torch.arange(N, dtype=torch.int32).reshape(1, N)
+    table[0, 7] = 10 ** 6                                # slot outside the cache -> skipped
+    idx = torch.full((n, 32), -1, dtype=torch.int32)
+    idx[1, :3] = torch.tensor([5, 7, 500])               # 7 -> bad slot, 500 -> past the table
+    idx[2, :2] = torch.tensor([5, 6])
+    out = torch.empty((n, h, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((n, h), dtype=torch.float32, device=DEV)
+    dsa.sparse_mla_prefill(q, kv.to(DEV), table.to(DEV), torch.zeros(n, dtype=torch.int32, device=DEV),
+                           idx.to(DEV), SM_SCALE, out, lse)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    assert (o[0] == 0).all() and (o[3] == 0).all() and np.isneginf(lse.cpu().numpy()[[0, 3]]).all()
+    np.testing.assert_array_equal(bits16(out)[1], np.broadcast_to(bits16(kv[5])[:512], (h, 512)))
+    ref_o, _ = oracle.sparse_mla(bits16(q.cpu()[2:3]), bits16(kv), idx[2:3].numpy(), SM_SCALE)
+    assert max_abs_rel(o[2:3], ref_o) <= TOL_BF16
+
+
+# ------------------------------------------------------------------ invariants
+def test_page_permutation_invariance():
+    """Identity vs shuffled page / slot layouts give bit-identical results."""
+    say("[invariance] page permutation")
+    L = 2000
+    a = run_prefill(synth.make_prefill(_cfg("C2", paged=False), L=L), 2048)
+    b = run_prefill(synth.make_prefill(_cfg("C2", paged=True), L=L), 2048)
+    causal = torch.arange(L, device=DEV)[None, :] <= torch.arange(L, device=DEV)[:, None]
+    assert torch.equal(a.scores[causal], b.scores[causal])      # columns past q_pos are never written
+    assert torch.equal(a.idx, b.idx)
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+
+
+def test_chunked_equals_monolithic():
+    """Chunked prefill against the growing cache reproduces the monolithic rows."""
+    say("[invariance] chunked == monolithic (fp8 kv)")
+    c = _cfg("C5", L=3072, chunk=1024)
+    inp = synth.make_prefill(c, L=3072, materialize_q=False)
+    mono = run_prefill(inp, c.k, kv_fp8=True)
+    st = P.alloc_prefill(inp.n_pages, c.d_i, inp.n_slots, c.chunk, 3072, c.k, c.h, kv_fp8=True)
+    d = lambda x: x.to(DEV)
+    for c0 in range(0, 3072, c.chunk):
+        c1 = c0 + c.chunk
+        P.store_tokens(st, d(inp.ik[c0:c1]), d(inp.ik_scale[c0:c1]), d(inp.ik_slot[c0:c1]), d(inp.kv[c0:c1]),
+                       d(inp.kv_slot_table[0, c0:c1]).long())
+        P.prefill_step(st, d(inp.iq[c0:c1]), d(inp.iq_scale[c0:c1]), d(inp.w[c0:c1]), d(inp.page_table),
+                       d(inp.kv_slot_table), d(inp.q_seq[c0:c1]), d(inp.q_pos[c0:c1]), d(inp.q_chunk(c0, c1)),
+                       c.k, SM_SCALE)
+        torch.cuda.synchronize()
+        m = inp.q_pos[c0:c1].numpy()
+        sc_chunk = st.scores.cpu().numpy()
+        sc_mono = mono.scores[c0:c1].cpu().numpy()
+        mask = np.arange(3072)[None, :] <= m[:, None]
+        assert np.array_equal(sc_chunk[mask], sc_mono[mask])
+        assert torch.equal(st.idx, mono.idx[c0:c1])
+        assert torch.equal(st.out.view(torch.int16), mono.out[c0:c1].view(torch.int16))
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("batch,lo,hi,n_splits", [(8, 2000, 9000, 0), (5, 100, 3000, 3), (3, 2049, 2049, 1)])
+def test_decode_vs_oracle(batch, lo, hi, n_splits):
+    say(f"[decode] B={batch} ctx=[{lo},{hi}] splits={n_splits}")
+    c = CONFIGS["C4"]
+    inp = synth.make_decode(c, batch=batch, ctx_lo=lo, ctx_hi=hi)
+    d = lambda x: x.to(DEV)
+    caches = P.alloc_prefill(inp.n_pages, c.d_i, inp.n_slots, 1, 1, c.k, c.h)
+    kv_slot = torch.empty(inp.n_slots, dtype=torch.int64)
+    for b in range(batch):
+        s0, nb = int(inp.seq_start[b]), int(inp.lens[b])
+        kv_slot[s0:s0 + nb] = inp.kv_slot_table[b, :nb].long()
+    P.store_tokens(caches, d(inp.ik), d(inp.ik_scale), d(inp.ik_slot), d(inp.kv), d(kv_slot))
+    ld = int(inp.lens.max())
+    ds = P.alloc_decode(batch, ld, c.k, c.h, n_splits=n_splits)
+    P.decode_step(ds, caches, d(inp.iq), d(inp.iq_scale), d(inp.w), d(inp.page_table), d(inp.kv_slot_table),
+                  d(inp.q_seq), d(inp.q_pos), d(inp.q), c.k, SM_SCALE)
+    torch.cuda.synchronize()
+    g = ds.scores.cpu().numpy()
+    pos = inp.q_pos.numpy()
+    ref = oracle.indexer_scores(u8(inp.iq), inp.iq_scale.numpy(), inp.w.numpy(), u8(inp.ik), inp.ik_scale.numpy(),
+                                pos, seq_start=inp.seq_start.numpy(), q_seq=inp.q_seq.numpy(), ld=ld,
+                                n_threads=oracle_threads())
+    mask = np.arange(ld)[None, :] <= pos[:, None]
+    for b in range(batch):
+        s0, nb = int(inp.seq_start[b]), int(inp.lens[b])
+        A = indexer_abs_scale(inp.iq[b:b + 1], inp.iq_scale[b:b + 1], inp.w[b:b + 1], inp.ik[s0:s0 + nb],
+                              inp.ik_scale[s0:s0 + nb], np.arange(1))
+        assert (np.abs(g[b, :nb] - ref[b, :nb]) <= BOUND_C * A[0] + 1e-30).all(), b
+    np.testing.assert_array_equal(ds.idx.cpu().numpy(), oracle.topk(g, pos, c.k))
+    idx = ds.idx.cpu().numpy()
+    ref_o, ref_l = oracle.sparse_mla(bits16(inp.q), bits16(inp.kv), idx, SM_SCALE,
+                                     seq_start=inp.seq_start.numpy(), q_seq=inp.q_seq.numpy(),
+                                     n_threads=oracle_threads())
+    e = max_abs_rel(ds.out.float().cpu().numpy(), ref_o)
+    say(f"  decode out max-abs-rel = {e:.3e}")
+    assert e <= TOL_BF16
+    assert float(np.abs(ds.lse.cpu().numpy() - ref_l).max()) <= 2e-2
+    # the prefill-form kernel on the same indices agrees within tolerance
+    out2 = torch.empty_like(ds.out)
+    dsa.sparse_mla_prefill(d(inp.q), caches.kv_cache, d(inp.kv_slot_table), d(inp.q_seq), ds.idx, SM_SCALE, out2)
+    torch.cuda.synchronize()
+    assert max_abs_rel(out2.float().cpu().numpy(), ref_o) <= TOL_BF16
+
+
+def test_decode_row_matches_prefill_row():
+    """A decode query at position N-1 equals the last prefill row of the same sequence."""
+    say("[invariance] decode row == prefill row")
+    c = _cfg("C2", paged=True)
+    L = 3000
+    inp = synth.make_prefill(c, L=L)
+    st = run_prefill(inp, c.k)
+    d = lambda x: x.to(DEV)
+    ds = P.alloc_decode(1, L, c.k, c.h)
+    P.decode_step(ds, st, d(inp.iq[-1:]), d(inp.iq_scale[-1:]), d(inp.w[-1:]), d(inp.page_table),
+                  d(inp.kv_slot_table), d(inp.q_seq[-1:]), d(inp.q_pos[-1:]), d(inp.q[-1:]), c.k, SM_SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(ds.scores[0], st.scores[L - 1])          # same per-pair arithmetic in both indexers
+    assert torch.equal(ds.idx[0], st.idx[L - 1])
+    assert max_abs_rel(ds.out[0].float().cpu().numpy(), st.out[L - 1].float().cpu().numpy()) <= 1e-2
