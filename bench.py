@@ -1,0 +1,335 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+Headline step (value): one prefill pass over a 32768-token sequence (B=1,
+causal, k=2048; indexer 64 heads x 128 FP8 keys in 64-token pages with a
+shuffled page table; MLA 128 heads, 576/512-d bf16 latent rows in a
+token-granular cache with shuffled slots):
+    cache stores -> indexer scores -> top-k -> sparse MLA prefill
+reported as prefill tokens/s.  Second figure: one decode step for 64
+sequences with contexts drawn uniformly from [32768, 131072] (one query
+each): cache stores -> indexer -> top-k -> sparse MLA decode, in us/step.
+
+All inputs are seeded synthetic tensors generated on the GPU before timing.
+Each stage is bracketed by HIP events on the stream the kernels run on; the
+roofline object uses the algorithmic work per launch divided by the measured
+average launch time.  The CPU baseline runs the oracle (the plain
+double-precision C reference) on a bounded sample of query rows of the same
+workload.
+
+HBM traffic of the dominant kernel comes from rocprofv3 counter runs
+(FETCH_SIZE, WRITE_SIZE) recorded in profiles/hbm_traffic.txt together with
+the SHA-256 of the kernel's sources; it is reported only while those sources
+are unchanged, otherwise as null.  --calib-copy adds one plain 1 GiB
+device-to-device copy after the timed work, the known-size kernel those
+counter runs are scaled by.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--calib-copy]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from synth.configs import CONFIGS, SM_SCALE  # noqa: E402
+import long_context_sparse_fp8_amd as dsa  # noqa: E402
+from long_context_sparse_fp8_amd import pipeline as P  # noqa: E402
+
+METRIC = "DSA prefill tokens/s at 32K & decode us/step at 128K ctx; % MFMA/HBM roofline"
+PEAK_FP8 = 5000.0      # TFLOP/s, dense MFMA (MI355X datasheet)
+PEAK_BF16 = 2500.0
+PEAK_HBM = 8000.0      # GB/s
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from profiles/hbm_traffic.txt, or None when
+    nothing is recorded or a source it was measured on has changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith("kernel="):
+            continue
+        f = dict(kv.split("=", 1) for kv in line.split())
+        if f.get("kernel") != kernel:
+            continue
+        for src, digest in zip(f["sources"].split(","), f["sha256"].split(",")):
+            path = os.path.join(ROOT, src)
+            if not os.path.exists(path) or hashlib.sha256(open(path, "rb").read()).hexdigest()[:16] != digest:
+                return None
+        return float(f["traffic_bytes"])
+    return None
+
+
+def calib_copy(dev, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size for scaling the HBM counters."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: {reps} x {nbytes} bytes")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class StageTimer:
+    """Per-stage HIP events on the current stream; averages over the timed steps."""
+
+    def __init__(self, names):
+        self.names = names
+        self.ev = {n: [] for n in names}
+
+    def mark(self, name):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        self.ev[name].append((s, e))
+        return e
+
+    def avg_ms(self):
+        torch.cuda.synchronize()
+        return {n: float(np.mean([s.elapsed_time(e) for s, e in v])) if v else 0.0 for n, v in self.ev.items()}
+
+
+# ---------------------------------------------------------------------------- prefill
+def prefill_work(L, k, h_i, d_i, h):
+    pairs = L * (L + 1) // 2
+    sel = sum(min(k, t + 1) for t in range(L))
+    return {
+        "indexer_flops": 2.0 * h_i * d_i * pairs,
+        "mla_flops": 2.0 * h * (576 + 512) * sel,
+        "topk_bytes": 4.0 * sum(t + 1 for t in range(L) if t + 1 > k) + 4.0 * L * k,
+        "selected_pairs": sel,
+        "pairs": pairs,
+    }
+
+
+def setup_prefill_c3(dev):
+    cfg = CONFIGS["C3"]
+    inp = synth.make_prefill(cfg, device=dev)
+    st = P.alloc_prefill(inp.n_pages, cfg.d_i, inp.n_slots, cfg.L, cfg.L, cfg.k, cfg.h, device=dev)
+    kv_slot = inp.kv_slot_table[0].long()
+    return cfg, inp, st, kv_slot
+
+
+def run_prefill_step(cfg, inp, st, kv_slot, timer=None):
+    def t(name):
+        return timer.mark(name) if timer else None
+
+    e = t("store")
+    P.store_tokens(st, inp.ik, inp.ik_scale, inp.ik_slot, inp.kv, kv_slot)
+    if e: e.record()
+    e = t("indexer")
+    dsa.indexer_scores(inp.iq, inp.iq_scale, inp.w, st.key_cache, st.key_scale, inp.page_table, inp.q_seq,
+                       inp.q_pos, st.scores)
+    if e: e.record()
+    e = t("topk")
+    dsa.topk(st.scores, inp.q_pos, cfg.k, st.idx)
+    if e: e.record()
+    e = t("mla")
+    dsa.sparse_mla_prefill(inp.q, st.kv_cache, inp.kv_slot_table, inp.q_seq, st.idx, SM_SCALE, st.out, st.lse)
+    if e: e.record()
+
+
+# ---------------------------------------------------------------------------- decode
+def setup_decode_c4(dev):
+    cfg = CONFIGS["C4"]
+    inp = synth.make_decode(cfg, device=dev)
+    caches = P.alloc_prefill(inp.n_pages, cfg.d_i, inp.n_slots, 1, 1, cfg.k, cfg.h, device=dev)
+    kv_slot = torch.empty(inp.n_slots, dtype=torch.int64)
+    kvt = inp.kv_slot_table.cpu()
+    for b in range(cfg.decode_batch):
+        s0, nb = int(inp.seq_start[b]), int(inp.lens[b])
+        kv_slot[s0:s0 + nb] = kvt[b, :nb].long()
+    kv_slot = kv_slot.to(dev)
+    P.store_tokens(caches, inp.ik, inp.ik_scale, inp.ik_slot, inp.kv, kv_slot)
+    # the step stores each sequence's newest token (its query position) again
+    last = (inp.seq_start + inp.lens - 1).to(dev)
+    newest = dict(ik=inp.ik[last], ik_scale=inp.ik_scale[last], ik_slot=inp.ik_slot[last], kv=inp.kv[last],
+                  kv_slot=kv_slot[last])
+    ld = int(inp.lens.max())
+    ds = P.alloc_decode(cfg.decode_batch, ld, cfg.k, cfg.h, device=dev)
+    torch.cuda.synchronize()
+    return cfg, inp, caches, newest, ds
+
+
+def run_decode_step(cfg, inp, caches, newest, ds, timer=None):
+    def t(name):
+        return timer.mark(name) if timer else None
+
+    e = t("store")
+    P.store_tokens(caches, newest["ik"], newest["ik_scale"], newest["ik_slot"], newest["kv"], newest["kv_slot"])
+    if e: e.record()
+    e = t("indexer")
+    dsa.indexer_scores(inp.iq, inp.iq_scale, inp.w, caches.key_cache, caches.key_scale, inp.page_table, inp.q_seq,
+                       inp.q_pos, ds.scores)
+    if e: e.record()
+    e = t("topk")
+    dsa.topk(ds.scores, inp.q_pos, cfg.k, ds.idx)
+    if e: e.record()
+    e = t("mla")
+    dsa.sparse_mla_decode(inp.q, caches.kv_cache, inp.kv_slot_table, inp.q_seq, ds.idx, SM_SCALE, ds.out, ds.lse,
+                          n_splits=ds.n_splits, ws=ds.ws)
+    if e: e.record()
+
+
+def decode_bytes(inp, k, h):
+    n_keys = int(inp.lens.sum())
+    return {
+        "indexer_bytes": n_keys * (128 + 4) + inp.iq.numel() + 4.0 * n_keys,   # keys + scales read, scores written
+        "topk_bytes": 4.0 * n_keys + 4.0 * inp.lens.numel() * k,
+        "mla_bytes": inp.lens.numel() * k * (1152 + 4 + 4) + inp.q.numel() * 2 + inp.lens.numel() * h * 512 * 2,
+    }
+
+
+# ---------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(inp, cfg, n_rows):
+    import oracle
+    rows = np.linspace(0, cfg.L - 1, n_rows).round().astype(np.int64)
+    u8 = lambda t: t.detach().cpu().contiguous().numpy().view(np.uint8)
+    b16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    iq, iqs, w = u8(inp.iq[rows]), inp.iq_scale[rows].cpu().numpy(), inp.w[rows].cpu().numpy()
+    ik, iks = u8(inp.ik), inp.ik_scale.cpu().numpy()
+    q, kv = b16(inp.q[rows]), b16(inp.kv)
+    pos = rows.astype(np.int32)
+    threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    sc = oracle.indexer_scores(iq, iqs, w, ik, iks, pos, ld=cfg.L, n_threads=threads)
+    idx = oracle.topk(sc, pos, cfg.k, n_threads=threads)
+    oracle.sparse_mla(q, kv, idx, SM_SCALE, n_threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": n_rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} evenly spaced query rows of the 32K prefill (positions 0..{cfg.L - 1}), full "
+                      f"indexer row + top-k + sparse MLA each, {dt:.1f} s wall on {threads} threads"}
+
+
+# ---------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dsa.lib()
+
+    # ---- prefill (headline)
+    log("[bench] generating the 32K prefill inputs on the GPU")
+    cfg, inp, st, kv_slot = setup_prefill_c3(dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        run_prefill_step(cfg, inp, st, kv_slot)
+    torch.cuda.synchronize()
+    log(f"[bench] prefill warmup done; timing {args.steps} steps")
+    timer = StageTimer(["store", "indexer", "topk", "mla"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_prefill_step(cfg, inp, st, kv_slot, timer)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    stages = timer.avg_ms()
+    ms_step = wall * 1e3
+    tok_s = cfg.L / wall
+    work = prefill_work(cfg.L, cfg.k, cfg.h_i, cfg.d_i, cfg.h)
+    idx_tf = work["indexer_flops"] / (stages["indexer"] * 1e-3) / 1e12
+    mla_tf = work["mla_flops"] / (stages["mla"] * 1e-3) / 1e12
+    topk_gbs = work["topk_bytes"] / (stages["topk"] * 1e-3) / 1e9
+    log(f"[bench] prefill {ms_step:.2f} ms/step, {tok_s:,.0f} tok/s; stages ms {stages}")
+    per_kernel = {
+        "indexer": {"bound": "mfma", "achieved": idx_tf, "peak": PEAK_FP8, "unit": "TFLOP/s",
+                    "frac": idx_tf / PEAK_FP8, "ms": stages["indexer"]},
+        "topk": {"bound": "hbm", "achieved": topk_gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                 "frac": topk_gbs / PEAK_HBM, "ms": stages["topk"]},
+        "sparse_mla_prefill": {"bound": "mfma", "achieved": mla_tf, "peak": PEAK_BF16, "unit": "TFLOP/s",
+                               "frac": mla_tf / PEAK_BF16, "ms": stages["mla"]},
+        "cache_store": {"ms": stages["store"]},
+    }
+    dom = max(("indexer", "topk", "sparse_mla_prefill"), key=lambda n: per_kernel[n]["ms"])
+    roof = {k2: v for k2, v in per_kernel[dom].items() if k2 != "ms"}
+    roof.update({"kernel": dom, "traffic": recorded_traffic(dom)})
+
+    result = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": "prefill B=1 L=32768 causal k=2048; indexer 64x128 FP8 keys, page 64, shuffled "
+                               "pages; sparse MLA 128 heads 576/512 bf16, page 1, shuffled slots",
+                   "global_batch": 1, "seq_len": cfg.L, "topk": cfg.k},
+        "stages_ms": stages,
+        "kernels": per_kernel,
+        "roofline": roof,
+    }
+
+    # ---- decode (second figure)
+    if not args.no_decode:
+        del st, inp
+        torch.cuda.empty_cache()
+        log("[bench] generating the 128K-context decode inputs on the GPU")
+        dcfg, dinp, caches, newest, ds = setup_decode_c4(dev)
+        for _ in range(args.warmup):
+            run_decode_step(dcfg, dinp, caches, newest, ds)
+        torch.cuda.synchronize()
+        dtimer = StageTimer(["store", "indexer", "topk", "mla"])
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run_decode_step(dcfg, dinp, caches, newest, ds, dtimer)
+        torch.cuda.synchronize()
+        dwall = (time.perf_counter() - t0) / args.steps
+        dst = dtimer.avg_ms()
+        db = decode_bytes(dinp, dcfg.k, dcfg.h)
+        dk = {
+            "indexer": {"bound": "hbm", "achieved": db["indexer_bytes"] / (dst["indexer"] * 1e-3) / 1e9,
+                        "peak": PEAK_HBM, "unit": "GB/s", "us": dst["indexer"] * 1e3},
+            "topk": {"bound": "hbm", "achieved": db["topk_bytes"] / (dst["topk"] * 1e-3) / 1e9, "peak": PEAK_HBM,
+                     "unit": "GB/s", "us": dst["topk"] * 1e3},
+            "sparse_mla_decode": {"bound": "hbm", "achieved": db["mla_bytes"] / (dst["mla"] * 1e-3) / 1e9,
+                                  "peak": PEAK_HBM, "unit": "GB/s", "us": dst["mla"] * 1e3},
+        }
+        for v in dk.values():
+            v["frac"] = v["achieved"] / v["peak"]
+        result["decode"] = {"workload": "decode: 64 sequences x 1 query, context ~ U[32768, 131072] "
+                                        f"(mean {float(dinp.lens.float().mean()):.0f}), k=2048, bf16 latent cache",
+                            "us_per_step": dwall * 1e6, "tokens_per_s": dcfg.decode_batch / dwall,
+                            "stages_us": {k2: v * 1e3 for k2, v in dst.items()}, "kernels": dk}
+        log(f"[bench] decode {dwall * 1e6:.1f} us/step; stages us {result['decode']['stages_us']}")
+        del caches, dinp, ds
+        torch.cuda.empty_cache()
+        inp = None
+
+    if args.calib_copy:
+        calib_copy(dev)
+
+    # ---- CPU baseline (the oracle on a bounded sample)
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a sample of query rows")
+        if inp is None:
+            cfg, inp, st, kv_slot = setup_prefill_c3(dev)
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
