@@ -225,7 +225,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
