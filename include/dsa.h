@@ -54,6 +54,7 @@ extern "C" {
 #define DSA_LATENT_DIM 576    /* latent key width: 512 value dims + 64 rope dims */
 #define DSA_VALUE_DIM 512     /* leading dims of a latent row that form the value */
 #define DSA_MAX_TOPK 2048
+#define DSA_MAX_TOPK_ROW 262144   /* longest score row dsa_topk accepts (scores_ld) */
 
 typedef enum dsa_status {
     DSA_OK = 0,
@@ -160,7 +161,8 @@ size_t dsa_topk_workspace_size(int32_t n_q, int64_t max_len, int32_t k);
  *   scores [n_q, scores_ld] fp32 (q_pos[t] < scores_ld is the caller's contract;
  *          columns at or beyond scores_ld are never read)
  *   idx    [n_q, k] int32
- * Supported: 1 <= k <= 2048. */
+ * Supported: 1 <= k <= 2048, scores_ld <= DSA_MAX_TOPK_ROW (DSA_ERR_UNSUPPORTED
+ * otherwise). */
 dsa_status dsa_topk(const float *scores, int64_t scores_ld, const int32_t *q_pos, int32_t n_q, int32_t k,
                     int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 

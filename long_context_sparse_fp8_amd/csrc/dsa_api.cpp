@@ -138,6 +138,8 @@ DSA_EXPORT dsa_status dsa_topk(const float *scores, int64_t scores_ld, const int
     REQUIRE(n_q >= 0, DSA_ERR_BAD_SHAPE, "dsa_topk: n_q = %d < 0", n_q);
     REQUIRE(k >= 1 && k <= DSA_MAX_TOPK, DSA_ERR_UNSUPPORTED, "dsa_topk: k = %d not in [1, %d]", k, DSA_MAX_TOPK);
     REQUIRE(scores_ld >= 1, DSA_ERR_BAD_SHAPE, "dsa_topk: scores_ld = %lld < 1", (long long)scores_ld);
+    REQUIRE(scores_ld <= DSA_MAX_TOPK_ROW, DSA_ERR_UNSUPPORTED, "dsa_topk: scores_ld = %lld > %d",
+            (long long)scores_ld, DSA_MAX_TOPK_ROW);
     REQUIRE(ws_bytes >= dsa_topk_workspace_size(n_q, scores_ld, k), DSA_ERR_WORKSPACE_TOO_SMALL,
             "dsa_topk: workspace too small");
     if (n_q == 0) return DSA_OK;

@@ -10,6 +10,10 @@ namespace dsa {
 // shape); larger calls use the query-blocked one (prefill shape).
 constexpr int kIndexerDecodeMaxQ = 256;
 
+// Top-k limits: k <= kTopkMaxK, score rows of at most kTopkMaxRow columns.
+constexpr int kTopkMaxK = 2048;
+constexpr int64_t kTopkMaxRow = 262144;
+
 struct IndexerArgs {
     const uint8_t *q_fp8;
     const float *q_scale;

@@ -6,14 +6,30 @@
 // row with no more than k candidates keeps all of them (the dense
 // degeneration of the deployment article, section 5.1).
 //
-// Scores become order-preserving uint32 keys.  Four MSB-first passes with
-// 8-bit digits find the k-th largest key T and how many keys equal to T must
-// be taken (`need`); the histograms live in LDS, one private copy per wave
-// so the ~16 busiest bins of a normal-shaped row do not serialize the whole
-// workgroup.  A final pass walks the row in index order and keeps keys > T
-// plus the first `need` keys == T, placing each kept index with wavefront
-// ballot / popcount prefix sums.  Everything is integer: the selection is
-// exact for the given scores.
+// One workgroup of 1024 threads per row; the work is bound by vector ALU
+// operations per score, so every score is touched by only three cheap sweeps:
+//   1. an 11-bit histogram of the top key bits (sign, exponent, two mantissa
+//      bits) in LDS, eight lane-interleaved copies; a block scan of the 2048
+//      bins from the top finds the bin holding the k-th largest key;
+//   2. the keys of that bin (a few percent of the row) are collected into an
+//      LDS candidate list, and the radix select finishes on the list alone
+//      (8-, 8- and 5-bit digits; it stops early once a bin is taken whole).
+//      Ties at the threshold key T are resolved by a second radix select over
+//      the candidates' indices: the `need` lowest indices equal to T are kept,
+//      i.e. every index up to a cut.  If the bin overflows the list (a row of
+//      mostly equal scores) the same passes run over the whole row instead;
+//   3. every kept score (key > T, or key == T at an index up to the cut) sets
+//      its bit in an LDS bitmap of the row; a block scan of the bitmap words'
+//      popcounts then writes the kept indices in ascending order.
+// Scores become order-preserving uint32 keys.  The row is cut into chunks of
+// 4096 scores; in chunk c thread i owns the four consecutive scores starting at
+// c * 4096 + 4 i, so every wave-wide load is one contiguous 1 KB run.  Rows of
+// at most 4096 * C scores are read once and kept in registers (every prefill
+// row here); longer rows are streamed chunk by chunk for each sweep (they are
+// few: one per decode sequence, and the re-reads hit L2).  Everything is
+// integer, so the selection is exact for the given scores.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -21,122 +37,368 @@ namespace dsa {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kChunk = 4 * kTopkThreads;        // scores per chunk
+constexpr int kBins0 = 2048;                    // first digit: key bits 31..21
+constexpr int kCopies0 = 8;                     // lane-interleaved copies of the first histogram
+constexpr int kCandCap = 8192;                  // candidate list capacity
+constexpr int kBins = 512;                      // later digits (<= 9 bits)
+constexpr int kCopies = 4;
+constexpr int kWords = (int)(kTopkMaxRow / 32); // bitmap words
 
-__device__ __forceinline__ uint32_t lane_prefix_count(uint64_t mask, int lane) {
-    return __builtin_popcountll(mask & ((1ull << lane) - 1ull));
+struct TopkSmem {
+    union {
+        uint32_t hist0[kBins0 * kCopies0];      // hist0[bin * 8 + lane % 8]
+        struct {
+            uint32_t key[kCandCap];
+            int32_t idx[kCandCap];
+        } cand;
+    };
+    uint32_t hist[kBins * kCopies];             // hist[bin * 4 + lane % 4]
+    uint32_t bitmap[kWords];
+    int32_t stage[kTopkMaxK];
+    uint32_t wsum[kTopkWaves];
+    uint32_t sel_bin, sel_rem, sel_done, n_cand;
+};
+
+// Block-wide exclusive scan (all 1024 threads call it); returns the sum over
+// lower threads, `total` gets the block sum.
+__device__ __forceinline__ uint32_t block_excl_scan(TopkSmem &sm, uint32_t a, uint32_t &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t ia = a;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(ia, o);
+        if (lane >= o) ia += u;
+    }
+    if (lane == 63) sm.wsum[wave] = ia;
+    __syncthreads();
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+        const uint32_t x = sm.wsum[w];
+        pre += w < wave ? x : 0u;
+        tot += x;
+    }
+    total = tot;
+    __syncthreads();   // wsum may be reused by the next scan
+    return pre + ia - a;
 }
 
+// Keys of one chunk for the calling thread: scores c*4096 + 4*tid + e, e = 0..3.
+// Branch-free: the load address is clamped into the row and keys past n are
+// zeroed afterwards, so every load of a row is issued before the first wait.
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(const float *row, int n, int c, uint32_t (&key)[4]) {
+    const int i = c * kChunk + 4 * (int)threadIdx.x;
+    float x[4];
+    if constexpr (VEC) {   // row 16-byte aligned; ceil4(n) <= ld
+        const float4 v = *reinterpret_cast<const float4 *>(row + min(i, ((n + 3) & ~3) - 4));
+        x[0] = v.x;
+        x[1] = v.y;
+        x[2] = v.z;
+        x[3] = v.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = row[min(i + e, n - 1)];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[e] = f32_order_key(x[e]) & (0u - (uint32_t)(i + e < n));
+}
+
+// Radix-select digit: counts are in sm.hist[bin * 4 + copy] for bins [0, nb).
+// Scans from the top (desc = true) or from the bottom and picks the bin that
+// holds the rem-th element.  Wave 0 only; the caller synchronises.  Kept out of
+// line: inlined, its reads get scheduled into the callers' loops and pin
+// registers for the whole kernel.
+__device__ __noinline__ void pick_digit(TopkSmem &sm, int nb, uint32_t rem, bool desc) {
+    const int lane = threadIdx.x & 63;
+    uint32_t c[8];   // lane owns 8 consecutive bins in scan order (nb <= 512)
+    uint32_t tot = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = 8 * lane + j;                  // rank in scan order
+        const int b = desc ? nb - 1 - r : r;
+        uint32_t s = 0;
+        if (r < nb) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(&sm.hist[b * kCopies]);
+            s = (v.x + v.y) + (v.z + v.w);
+        }
+        c[j] = s;
+        tot += s;
+    }
+    uint32_t incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(incl, o);
+        if (lane >= o) incl += u;
+    }
+    uint32_t excl = incl - tot;
+    if (excl < rem && incl >= rem) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (excl < rem && excl + c[j] >= rem) {
+                const int r = 8 * lane + j;
+                sm.sel_bin = (uint32_t)(desc ? nb - 1 - r : r);
+                sm.sel_rem = rem - excl;
+                sm.sel_done = (excl + c[j] == rem) ? 1u : 0u;   // the whole bin is taken
+            }
+            excl += c[j];
+        }
+    }
+}
+
+// C > 0: rows of at most C chunks, keys held in registers.  C == 0: chunks are
+// streamed from memory in every sweep.
+template <int C, bool VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
                                                              const int32_t *__restrict__ q_pos, int32_t k,
                                                              int32_t *__restrict__ idx) {
-    __shared__ uint32_t hist[kTopkWaves][256];
-    __shared__ uint32_t total[256];
-    __shared__ uint32_t sel_bin, sel_rem;
-    __shared__ uint32_t wcnt[2][kTopkWaves];
-
+    __shared__ __attribute__((aligned(16))) TopkSmem sm;
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int64_t n = (int64_t)q_pos[t] + 1;
-    if (n > ld) n = ld;
-    if (n < 0) n = 0;
-    const float *row = scores + (int64_t)t * ld;
+    int64_t n64 = (int64_t)q_pos[t] + 1;
+    if (n64 > ld) n64 = ld;
+    if (n64 < 0) n64 = 0;
+    const int n = (int)n64;   // n <= ld <= kTopkMaxRow (checked by the API)
     int32_t *out = idx + (int64_t)t * k;
 
     if (n <= k) {   // every candidate is kept
         for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
         return;
     }
+    const float *row = scores + (int64_t)t * ld;
+    const int nc = (n + kChunk - 1) / kChunk;   // chunks of this row (uniform)
 
-    uint32_t prefix = 0, pmask = 0, rem = (uint32_t)k;   // rem: how many still to take at/below the prefix
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
-        __syncthreads();
-        for (int64_t i = tid; i < n; i += kTopkThreads) {
-            const uint32_t key = f32_order_key(row[i]);
-            if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (tid < 256) {
-            uint32_t s = 0;
+    uint32_t reg[C > 0 ? C : 1][4];
+    if constexpr (C > 0) {
 #pragma unroll
-            for (int wv = 0; wv < kTopkWaves; ++wv) s += hist[wv][tid];
-            total[tid] = s;
-        }
-        __syncthreads();
-        // bins from the top: find the bin holding the rem-th largest key.
-        // Threads 0..255 (4 waves) own bin 255 - tid: an inclusive scan within
-        // each wave, then the preceding waves' totals are added.
-        uint32_t v = 0, incl = 0;
-        if (tid < 256) {
-            v = total[255 - tid];
-            incl = v;
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t u = __shfl_up(incl, o);
-                if (lane >= o) incl += u;
-            }
-            if (lane == 63) wcnt[0][wave] = incl;
-        }
-        __syncthreads();
-        if (tid < 256) {
-            for (int wv = 0; wv < wave; ++wv) incl += wcnt[0][wv];
-            const uint32_t excl = incl - v;
-            if (excl < rem && incl >= rem) {
-                sel_bin = 255u - (uint32_t)tid;
-                sel_rem = rem - excl;
+        for (int c = 0; c < C; ++c) {
+            if (c < nc) {
+                load_chunk<VEC>(row, n, c, reg[c]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) reg[c][e] = 0u;
             }
         }
-        __syncthreads();
-        const uint32_t b = sel_bin;
-        rem = sel_rem;
-        prefix |= b << shift;
-        pmask |= 255u << shift;
-        __syncthreads();
     }
-    const uint32_t T = prefix;
-    const uint32_t need = rem;       // keys equal to T to take, lowest indices first
+    // fn(key, index) for every score of the row owned by this thread.  Slots past
+    // n hold key 0; with CHECK they are skipped, without it they are passed on
+    // (register form only), which keeps the per-slot range test out of the hot
+    // sweeps: key 0 falls below every threshold unless the threshold bin is bin 0,
+    // and the callers switch to CHECK exactly then.
+    auto each_key = [&](auto check, auto fn) {
+        constexpr bool CHECK = decltype(check)::value;
+        if constexpr (C > 0) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if (c < nc) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = c * kChunk + 4 * tid + e;
+                        if (!CHECK || i < n) fn(reg[c][e], i);
+                    }
+                }
+            }
+        } else {
+            for (int c = 0; c < nc; ++c) {
+                uint32_t key[4];
+                load_chunk<VEC>(row, n, c, key);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = c * kChunk + 4 * tid + e;
+                    if (i < n) fn(key[e], i);
+                }
+            }
+        }
+    };
+    using Checked = std::integral_constant<bool, true>;
+    using Unchecked = std::integral_constant<bool, false>;
+    auto clear = [&](uint32_t *p, int words) {
+        for (int i = tid; i < words / 4; i += kTopkThreads) reinterpret_cast<uint4 *>(p)[i] = make_uint4(0, 0, 0, 0);
+    };
 
-    // ordered compaction
-    uint32_t eq_seen = 0, out_pos = 0;
-    for (int64_t base = 0; base < n; base += kTopkThreads) {
-        const int64_t i = base + tid;
-        uint32_t key = 0;
-        if (i < n) key = f32_order_key(row[i]);
-        const bool gt = i < n && key > T;
-        const bool eq = i < n && key == T;
-        const uint64_t beq = __ballot(eq);
-        if (lane == 0) wcnt[0][wave] = (uint32_t)__builtin_popcountll(beq);
-        __syncthreads();
-        uint32_t eq_before = eq_seen;
-        uint32_t eq_chunk = 0;
-        for (int wv = 0; wv < kTopkWaves; ++wv) {
-            const uint32_t c = wcnt[0][wv];
-            if (wv < wave) eq_before += c;
-            eq_chunk += c;
-        }
-        eq_before += lane_prefix_count(beq, lane);
-        const bool sel = gt || (eq && eq_before < need);
-        const uint64_t bsel = __ballot(sel);
-        if (lane == 0) wcnt[1][wave] = (uint32_t)__builtin_popcountll(bsel);
-        __syncthreads();
-        uint32_t pos = out_pos, sel_chunk = 0;
-        for (int wv = 0; wv < kTopkWaves; ++wv) {
-            const uint32_t c = wcnt[1][wv];
-            if (wv < wave) pos += c;
-            sel_chunk += c;
-        }
-        pos += lane_prefix_count(bsel, lane);
-        if (sel && pos < (uint32_t)k) out[pos] = (int32_t)i;
-        eq_seen += eq_chunk;
-        out_pos += sel_chunk;
-        __syncthreads();
-        if (out_pos >= (uint32_t)k) break;
+    // ---- sweep 1: 11-bit histogram of the top key bits
+    clear(sm.hist0, kBins0 * kCopies0);
+    __syncthreads();
+    {
+        uint32_t *h = sm.hist0 + (lane & (kCopies0 - 1));
+        each_key(Unchecked{}, [&](uint32_t key, int) { atomicAdd(&h[(key >> 21) * kCopies0], 1u); });
     }
+    __syncthreads();
+    uint32_t rem;
+    uint32_t b0;
+    {
+        // thread tid owns bins 2047 - 2 tid and 2046 - 2 tid (scan order: descending)
+        uint32_t ca = 0, cb = 0;
+        const uint4 *pa = reinterpret_cast<const uint4 *>(sm.hist0 + (kBins0 - 1 - 2 * tid) * kCopies0);
+        const uint4 *pb = reinterpret_cast<const uint4 *>(sm.hist0 + (kBins0 - 2 - 2 * tid) * kCopies0);
+        const uint4 a0 = pa[0], a1 = pa[1], c0 = pb[0], c1 = pb[1];
+        ca = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w));
+        cb = ((c0.x + c0.y) + (c0.z + c0.w)) + ((c1.x + c1.y) + (c1.z + c1.w));
+        if (C > 0 && tid == kTopkThreads - 1) cb -= (uint32_t)(nc * kChunk - n);   // padding keys in bin 0
+        uint32_t total;
+        const uint32_t excl = block_excl_scan(sm, ca + cb, total);
+        const uint32_t kk = (uint32_t)k;
+        if (excl < kk && excl + ca + cb >= kk) {
+            if (excl + ca >= kk) {
+                sm.sel_bin = (uint32_t)(kBins0 - 1 - 2 * tid);
+                sm.sel_rem = kk - excl;
+                sm.sel_done = (excl + ca == kk) ? 1u : 0u;
+            } else {
+                sm.sel_bin = (uint32_t)(kBins0 - 2 - 2 * tid);
+                sm.sel_rem = kk - excl - ca;
+                sm.sel_done = (excl + ca + cb == kk) ? 1u : 0u;
+            }
+        }
+        __syncthreads();
+        b0 = sm.sel_bin;
+        rem = sm.sel_rem;
+    }
+    bool done = sm.sel_done != 0;
+    uint32_t prefix = b0 << 21, pmask = 0xFFE00000u;
+    // padding keys (0) can only tie with a threshold in bin 0
+    auto each_row = [&](auto fn) {
+        if (b0 == 0) each_key(Checked{}, fn);
+        else each_key(Unchecked{}, fn);
+    };
+
+    // ---- sweep 2: collect the threshold bin's keys (unless it is taken whole)
+    bool use_list = false;
+    uint32_t n_cand = 0;
+    if (!done) {
+        uint32_t mine = 0;
+        each_row([&](uint32_t key, int) { mine += (key >> 21) == b0 ? 1u : 0u; });
+        uint32_t total;
+        uint32_t pos = block_excl_scan(sm, mine, total);   // also orders hist0 reads before the list writes
+        n_cand = total;
+        use_list = total <= (uint32_t)kCandCap;
+        if (use_list) {
+            each_row([&](uint32_t key, int i) {
+                if ((key >> 21) == b0) {
+                    sm.cand.key[pos] = key;
+                    sm.cand.idx[pos] = i;
+                    ++pos;
+                }
+            });
+        }
+        __syncthreads();
+    }
+    // fn(key, index) over the elements still in play: the candidate list, or (a
+    // row of mostly equal scores that overflows the list) the whole row, re-read
+    // from memory so that the register copy stays out of the pass loops
+    auto each_live = [&](auto fn) {
+        if (use_list) {
+            for (int j = tid; j < (int)n_cand; j += kTopkThreads) fn(sm.cand.key[j], sm.cand.idx[j]);
+        } else {
+            for (int c = 0; c < nc; ++c) {
+                uint32_t key[4];
+                load_chunk<VEC>(row, n, c, key);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = c * kChunk + 4 * tid + e;
+                    if (i < n) fn(key[e], i);
+                }
+            }
+        }
+    };
+    uint32_t *hc = sm.hist + (lane & (kCopies - 1));
+
+    // ---- finish the key select on the live set: digits 8, 8, 5 below the first 11 bits
+    if (!done) {
+#pragma unroll 1
+        for (int pass = 0; pass < 3 && !done; ++pass) {
+            const int shift = pass == 0 ? 13 : (pass == 1 ? 5 : 0);
+            const int width = pass == 2 ? 5 : 8;
+            const uint32_t dmask = (1u << width) - 1u;
+            clear(sm.hist, kBins * kCopies);
+            __syncthreads();
+            each_live([&](uint32_t key, int) {
+                if ((key & pmask) == prefix) atomicAdd(&hc[((key >> shift) & dmask) * kCopies], 1u);
+            });
+            __syncthreads();
+            if (wave == 0) pick_digit(sm, 1 << width, rem, true);
+            __syncthreads();
+            prefix |= sm.sel_bin << shift;
+            pmask |= dmask << shift;
+            rem = sm.sel_rem;
+            done = sm.sel_done != 0;
+            __syncthreads();
+        }
+    }
+    // keys with (key & pmask) > prefix are kept; of those equal to it, the `rem`
+    // lowest indices: every index <= cut
+    int cut = 0x7FFFFFFF;
+    if (!done) {
+        // radix select of the rem-th smallest index among keys equal to prefix
+        // (indices < 2^18: digits 9 + 9)
+        uint32_t ipre = 0, imask = 0;
+#pragma unroll 1
+        for (int pass = 0; pass < 2; ++pass) {
+            const int shift = pass == 0 ? 9 : 0;
+            clear(sm.hist, kBins * kCopies);
+            __syncthreads();
+            each_live([&](uint32_t key, int i) {
+                if ((key & pmask) == prefix && ((uint32_t)i & imask) == ipre)
+                    atomicAdd(&hc[(((uint32_t)i >> shift) & 511u) * kCopies], 1u);
+            });
+            __syncthreads();
+            if (wave == 0) pick_digit(sm, kBins, rem, false);
+            __syncthreads();
+            ipre |= sm.sel_bin << shift;
+            imask |= 511u << shift;
+            rem = sm.sel_rem;
+            __syncthreads();
+        }
+        cut = (int)ipre;
+    }
+
+    // ---- sweep 3: bitmap of the kept indices, then ordered output
+    const int nwords = (n + 31) >> 5;
+    clear(sm.bitmap, (nwords + 3) & ~3);
+    __syncthreads();
+    each_row([&](uint32_t key, int i) {
+        const uint32_t km = key & pmask;
+        if (km > prefix || (km == prefix && i <= cut)) atomicOr(&sm.bitmap[i >> 5], 1u << (i & 31));
+    });
+    __syncthreads();
+    {
+        const int W = (nwords + kTopkThreads - 1) / kTopkThreads;   // words per thread, in order
+        const int w0 = min(nwords, tid * W), w1 = min(nwords, w0 + W);
+        uint32_t cnt = 0;
+        for (int w = w0; w < w1; ++w) cnt += (uint32_t)__builtin_popcount(sm.bitmap[w]);
+        uint32_t total;
+        uint32_t pos = block_excl_scan(sm, cnt, total);
+        for (int w = w0; w < w1; ++w) {
+            uint32_t bits = sm.bitmap[w];
+            while (bits) {
+                const int b = __builtin_ctz(bits);
+                bits &= bits - 1;
+                if (pos < (uint32_t)k) sm.stage[pos] = 32 * w + b;   // exactly k are kept
+                ++pos;
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = sm.stage[i];
 }
 
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k, int32_t *idx,
                        hipStream_t stream) {
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)n_q), dim3(kTopkThreads), 0, stream, scores, ld, q_pos, k, idx);
+    const dim3 grid((unsigned)n_q), block(kTopkThreads);
+    // scores is 16-byte aligned (checked by the API), so rows are when ld % 4 == 0
+    if ((ld & 3) == 0) {
+        if (ld <= 4 * kChunk)
+            hipLaunchKernelGGL((topk_kernel<4, true>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
+        else if (ld <= 8 * kChunk)
+            hipLaunchKernelGGL((topk_kernel<8, true>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
+        else
+            hipLaunchKernelGGL((topk_kernel<0, true>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
+    } else {
+        if (ld <= 8 * kChunk)
+            hipLaunchKernelGGL((topk_kernel<8, false>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
+        else
+            hipLaunchKernelGGL((topk_kernel<0, false>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
+    }
     return hipGetLastError();
 }
 

@@ -71,7 +71,11 @@ class DecodeState:
 
 
 def alloc_decode(batch, ld, k, h, n_splits=0, device="cuda"):
+    """Buffers of one decode step over contexts of up to `ld` tokens.  The score
+    rows are padded to a multiple of 64 columns so every row is 256-byte aligned
+    (the top-k then reads them with 16-byte vector loads)."""
     need = B.sparse_mla_decode_workspace_size(batch, h, k, n_splits)
+    ld = (ld + 63) // 64 * 64
     return DecodeState(scores=torch.empty((batch, ld), dtype=torch.float32, device=device),
                        idx=torch.empty((batch, k), dtype=torch.int32, device=device),
                        out=torch.empty((batch, h, B.DV), dtype=torch.bfloat16, device=device),

@@ -75,6 +75,8 @@ def test_topk_validation(L):
     assert L.dsa_topk(A, 100, A, 4, 0, A, None, 0, None) == 3
     assert L.dsa_topk(A, 100, A, 4, 2049, A, None, 0, None) == 3
     assert L.dsa_topk(A, 0, A, 4, 16, A, None, 0, None) == 2
+    assert L.dsa_topk(A, 262144, A, 4, 16, MIS, None, 0, None) == 4   # longest row accepted; MIS trips next
+    assert L.dsa_topk(A, 262145, A, 4, 16, A, None, 0, None) == 3    # beyond DSA_MAX_TOPK_ROW
     assert L.dsa_topk(None, 100, A, 4, 16, A, None, 0, None) == 1
     assert L.dsa_topk(A, 100, A, 4, 16, MIS, None, 0, None) == 4
     assert L.dsa_topk_workspace_size(4, 100, 16) == 0
