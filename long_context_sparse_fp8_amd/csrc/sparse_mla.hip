@@ -6,20 +6,29 @@
 //   l_s = sm_scale * q[t,h,:] . K[s,:]   (576-d latent keys)
 //   out[t,h,:] = softmax(l) @ K[S_t, :512],  lse[t,h] = log sum exp(l)
 //
-// One workgroup per query (decode: per query and index split); every wave
-// owns 16 heads, so 128 heads are 8 waves (2 per SIMD) and Q^T (72 VGPRs)
-// plus the fp32 O^T accumulator (128) stay in registers for the whole query.
-// Per 64-row tile:
+// One workgroup per query (decode: per query and index split).  Every wave
+// owns 32 heads, so 128 heads are 4 waves, one per SIMD; Q^T (144 VGPRs) and
+// the fp32 O^T accumulator (256) stay in registers for the whole query.  Each
+// gathered row is read from memory once per query and shared by all heads
+// through LDS.  Per 64-row tile:
 //   * the selected rows are gathered straight into LDS with
 //     global_load_lds_dwordx4 (no register staging), double-buffered, rows
-//     padded to 1168 bytes so both the row reads and the transposed reads
-//     below are bank-conflict free;
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = 16 gathered rows from LDS,
-//     B = the wave's 16 query heads held in VGPRs);
-//   * online softmax per head (= per lane column), exp2 domain;
+//     padded to 1168 bytes and the MFMA rows mapped to tile rows so that both
+//     the row reads and the transposed reads below are bank-conflict free;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 gathered rows from LDS,
+//     B = the wave's 32 query heads held in VGPRs): each 16-byte LDS fragment
+//     feeds 32 heads, which halves LDS traffic per flop against 16-head tiles;
+//   * softmax per head (= per lane column) in the exp2 domain against a fixed
+//     reference: the head's maximum over its first tile.  Probabilities of later
+//     tiles may exceed 1 by up to 2^64 before the reference must move; that
+//     range is exact in fp32 sums and bf16 probabilities, and the final division
+//     gives the same softmax as a running-max rescale.  A tile beyond it restarts
+//     the query with a raised reference instead of rescaling the accumulators,
+//     which keeps O^T in accumulation registers that VALU code never touches;
 //   * O^T += V^T P^T: P^T is the S^T accumulator re-packed to bf16 in place
-//     (its lane layout already is the B operand), V^T comes from the same LDS
-//     tile through ds_read_b64_tr_b16 transposed reads.
+//     (its lane layout already is the B operand, with the k index permuted
+//     consistently on both operands), V^T comes from the same LDS tile through
+//     ds_read_b64_tr_b16 transposed reads.
 // FP8 rows (E4M3 + per-row scale) are gathered as bytes, expanded to bf16 in
 // LDS exactly, and their scale is applied to the logits and to P in fp32.
 #include "dsa_device.h"
@@ -34,8 +43,11 @@ constexpr int kTileB = kTile * kRowB;             // 74752 bytes
 constexpr int kF8RowC = kDk / 16;                 // 16-byte chunks per FP8 row (36)
 constexpr int kF8TileB = kTile * kDk;             // 36864 bytes
 constexpr int kMaxK = 2048;
+constexpr int kKSteps = kDk / 16;                 // 36 k-steps of 16 latent dims
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLook = 4;                          // LDS fragment loads in flight per wave
+constexpr float kHeadroom = 64.0f;                // log2 range allowed above a head's reference max
+constexpr int kLookK = 4;                         // K fragments in flight per wave
+constexpr int kLookV = 4;                         // V^T fragments in flight per wave
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -53,15 +65,32 @@ __device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
+__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Tile rows are padded to 1168 bytes (73 16-byte chunks): 16 consecutive rows
+// then start on 16 distinct chunk columns modulo 16, so the row reads (16 lanes =
+// 16 rows x 16 bytes per cycle on gfx950's 64 banks) are conflict-free.  The
+// transposed reads fetch 4 rows x 32 bytes per 16-lane group; they are
+// conflict-free when those 4 rows are 4 apart.  So the MFMA row index rho (the
+// S^T accumulator row, and the k index of the PV product) maps to the tile row
+// tau(rho) that transposes the 4x4 blocks of every 16 rows:
+//   tau(16 B + 4 a + b) = 16 B + 4 b + a,
+// under which each transposed read's 4 consecutive k slots are tile rows 4
+// apart, and every fragment address is one per-lane base plus a constant.
+__device__ __forceinline__ int tau(int rho) { return (rho & ~15) | ((rho & 3) << 2) | ((rho >> 2) & 3); }
+
+// Tile buffers live in separate __shared__ arrays, each named statically at every
+// use, so that the compiler can tell the asynchronous gather into one buffer from
+// the reads of the other and does not make the reads wait for the gather.
 template <int NW, bool FP8, bool SPLIT>
 struct MlaSmem {
-    // bf16 tiles: two for the bf16 cache (double buffer), one for FP8 (filled by conversion)
-    uint8_t tile[FP8 ? 1 : 2][kTileB];
-    uint8_t f8[FP8 ? 2 : 1][FP8 ? kF8TileB : 16];
     float f8scale[FP8 ? kTile : 1];
     int32_t slots[kMaxK];
     uint32_t wcount[NW];
     int32_t n_valid;
+    uint32_t restart;
 };
 
 template <int NW, bool FP8, bool SPLIT>
@@ -73,15 +102,22 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     constexpr int NT = NW * 64;
     constexpr int R = (kMaxK + NT - 1) / NT;      // index entries per thread
     __shared__ __attribute__((aligned(16))) MlaSmem<NW, FP8, SPLIT> sm;
+    // bf16 cache: tile_a / tile_b double buffer.  FP8 cache: codes staged in
+    // f8_a / f8_b (double buffer), expanded into tile_a.
+    __shared__ __attribute__((aligned(16))) uint8_t tile_a[kTileB];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_b[FP8 ? 16 : kTileB];
+    __shared__ __attribute__((aligned(16))) uint8_t f8_a[FP8 ? kF8TileB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t f8_b[FP8 ? kF8TileB : 16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int G = lane >> 4, i16 = lane & 15;     // 16-lane group, lane within it
+    const int g = lane >> 5, l32 = lane & 31;     // lane half, lane within the half
+    const int i16 = lane & 15, hd = (lane >> 4) & 1;
     const int t = SPLIT ? (int)blockIdx.x / n_splits : (int)blockIdx.x;
     const int split = SPLIT ? (int)blockIdx.x % n_splits : 0;
     const int per_split = SPLIT ? (k + n_splits - 1) / n_splits : k;
     const int i_begin = split * per_split;
     const int i_end = min(k, i_begin + per_split);
-    const int head = 16 * wave + i16;
+    const int head = 32 * wave + l32;
     const bool head_ok = head < h;
 
     // ---- resolve the selected rows to cache slots, compacted in index order
@@ -122,39 +158,42 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
             base += tot;
             __syncthreads();
         }
-        if (tid == 0) sm.n_valid = base;
+        if (tid == 0) {
+            sm.n_valid = base;
+            sm.restart = 0;
+        }
     }
     __syncthreads();
     const int n_valid = sm.n_valid;
     const int n_tiles = (n_valid + kTile - 1) / kTile;
 
-    // ---- Q^T fragments of this wave's 16 heads (B operand, K = 576 in 18 steps of 32)
-    bf16x8 qf[18];
+    // ---- Q^T fragments of this wave's 32 heads (B operand): k-step ks holds
+    // latent dims 16 ks + 8 g .. +8 of head `head`
+    bf16x8 qf[kKSteps];
     {
-        const uint16_t *qrow = q + ((int64_t)t * h + (head_ok ? head : 0)) * kDk + 8 * G;
+        const uint16_t *qrow = q + ((int64_t)t * h + (head_ok ? head : 0)) * kDk + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
+        for (int ks = 0; ks < kKSteps; ++ks) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (head_ok) v = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
+            if (head_ok) v = *reinterpret_cast<const uint4 *>(qrow + 16 * ks);
             qf[ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
 
-    // ---- tile gather (asynchronous, straight to LDS)
-    auto gather = [&](int j, int buf) {
+    // ---- tile gather (asynchronous, straight to LDS, swizzled through the source addresses)
+    auto gather = [&](int j, uint8_t *dst) {
         const int row0 = j * kTile;
         const uint8_t *kvb = reinterpret_cast<const uint8_t *>(kv_cache);
         if constexpr (!FP8) {
-            uint8_t *dst = sm.tile[buf];
             for (int ins = wave; ins < kRowC; ins += NW) {   // 73 wave-wide 1 KB copies
                 const int c = ins * 64 + lane;
                 const int r = c / kRowC, col = c - r * kRowC;
                 const int rr = row0 + r < n_valid ? row0 + r : 0;
                 const int64_t sl = sm.slots[rr];
+                // the pad chunk (col 72) takes a duplicate of chunk 71
                 g2lds16(kvb + sl * (kDk * 2) + (col < kRowC - 1 ? col : kRowC - 2) * 16, to_lds(dst + ins * 1024));
             }
         } else {
-            uint8_t *dst = sm.f8[buf];
             for (int ins = wave; ins < kF8RowC; ins += NW) {  // 36 wave-wide 1 KB copies
                 const int c = ins * 64 + lane;
                 const int r = c / kF8RowC, col = c - r * kF8RowC;
@@ -165,12 +204,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         }
     };
     // FP8: expand the staged codes of tile j into the bf16 tile (exact), fetch row scales
-    auto expand = [&](int j, int buf) {
+    auto expand = [&](int j, const uint8_t *src, uint8_t *dst_tile) {
         if constexpr (FP8) {
             const int row0 = j * kTile;
             for (int c = tid; c < kTile * kF8RowC; c += NT) {
                 const int r = c / kF8RowC, col = c - r * kF8RowC;
-                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.f8[buf][r * kDk + col * 16]);
+                const uint4 v = *reinterpret_cast<const uint4 *>(&src[r * kDk + col * 16]);
                 const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
                 uint32_t o8[8];
 #pragma unroll
@@ -182,7 +221,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                     o8[2 * e] = __builtin_bit_cast(uint32_t, b0);
                     o8[2 * e + 1] = __builtin_bit_cast(uint32_t, b1);
                 }
-                uint4 *d = reinterpret_cast<uint4 *>(&sm.tile[0][r * kRowB + col * 32]);
+                uint4 *d = reinterpret_cast<uint4 *>(&dst_tile[r * kRowB + col * 32]);
                 d[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
                 d[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
             }
@@ -193,136 +232,182 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         }
     };
 
-    // O^T accumulators: tile dt holds dims 16 dt + 4 G + i of head `head`
-    f32x4 o[32];
+    // Per-lane LDS byte offsets within a tile.  K fragment (k-step ks, half hf): tile
+    // row tau(l32) + 32 hf, dims 16 ks + 8 g  -> k_base + 32 hf rows + 32 ks bytes.
+    // V^T fragment (k-step kk, dim tile dt): k slots 8 g + e (e < 4) are rho =
+    // 16 kk + 4 g + e (lo) and rho + 8 (hi), i.e. tile rows 16 kk + 4 e + g and
+    // 16 kk + 4 e + g + 2; lane i16 of a 16-lane group supplies row e = i16 / 4,
+    // dims 32 dt + 16 hd + 4 (i16 % 4)  -> v_base + 16 kk rows + 64 dt bytes (+2 rows).
+    const int k_base = tau(l32) * kRowB + 16 * g;
+    const int v_base = (4 * (i16 >> 2) + g) * kRowB + 32 * hd + 8 * (i16 & 3);
+
+    // O^T accumulators: o[dt][i] holds latent dim 32 dt + 8 (i / 4) + 4 g + i % 4 of head `head`
+    f32x16 o[16];
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) o[dt] = f32x4{0, 0, 0, 0};
-    float m_run = -INFINITY, l_run = 0.0f;
+    for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
+    // Softmax reference: each head's maximum over its first tile.  Later tiles are
+    // exponentiated against it as long as their maximum stays within kHeadroom
+    // (log2 units) of it, which fp32 sums and bf16 probabilities hold exactly as
+    // the rescaled form would; a tile beyond that restarts the query with the
+    // larger reference, so the accumulators are never rescaled.
+    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
     const float c2 = sm_scale * kLog2e;
 
-    if (n_tiles > 0) gather(0, 0);
-    for (int j = 0; j < n_tiles; ++j) {
-        const int buf = j & 1;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();                                  // tile j landed; everyone is done with tile j-1
-        if (j + 1 < n_tiles) gather(j + 1, FP8 ? buf ^ 1 : buf ^ 1);
-        if constexpr (FP8) {
-            expand(j, buf);
-            __syncthreads();
-        }
-        const uint8_t *tile = sm.tile[FP8 ? 0 : buf];
+    // Attempts: the second and later ones only run after a tile exceeded its head's
+    // reference by more than kHeadroom (practically never); they restart from tile
+    // 0 with every reference raised to the largest maximum seen so far.
+    bool again = true;
+    while (again) {
+        // one tile: `cur` holds tile j (bf16 rows, or FP8 codes to expand), the gather
+        // of tile j + 1 goes to `nxt`; returns true when the query must restart
+        auto step = [&](const int j, uint8_t *cur, uint8_t *nxt) -> bool {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                              // tile j landed; everyone is done with tile j-1
+            if (sm.restart != 0) return true;             // workgroup-uniform; nothing is in flight
+            if (j + 1 < n_tiles) gather(j + 1, nxt);
+            const uint8_t *tile = cur;
+            if constexpr (FP8) {
+                expand(j, cur, tile_a);
+                __syncthreads();
+                tile = tile_a;
+            }
 
-        // S^T = K Q^T : four 16-row subtiles; element i of subtile n is row 16 n + 4 G + i.
-        // The 72 (subtile, k-step) fragment loads run kLook steps ahead of their MFMA
-        // in a register ring; the scheduling barriers keep that order so the live
-        // register set stays bounded (Q^T and O^T already hold 200 VGPRs).
-        f32x4 s[4];
+            // S^T = K Q^T: s[hf] covers rho = 32 hf + 8 (i / 4) + 4 g + i % 4.  The 72
+            // (k-step, half) fragment loads run kLookK steps ahead of their MFMA in a
+            // register ring; the scheduling barriers keep that order.
+            f32x16 s[2];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) s[n] = f32x4{0, 0, 0, 0};
-        {
-            const uint8_t *kbase = tile + i16 * kRowB + 16 * G;
-            auto kload = [&](int f) {
-                return *reinterpret_cast<const uint4 *>(kbase + (f / 18) * 16 * kRowB + 64 * (f % 18));
-            };
-            uint4 ring[kLook];
+            for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int f = 0; f < kLook; ++f) ring[f] = kload(f);
+                for (int i = 0; i < 16; ++i) s[hf][i] = 0.0f;
+            {
+                const uint8_t *kb = tile + k_base;
+                auto kload = [&](int f) {
+                    return *reinterpret_cast<const uint4 *>(kb + (f & 1) * 32 * kRowB + 32 * (f >> 1));
+                };
+                uint4 ring[kLookK];
 #pragma unroll
-            for (int f = 0; f < 72; ++f) {
-                const uint4 cur = ring[f % kLook];
-                if (f + kLook < 72) ring[f % kLook] = kload(f + kLook);
-                s[f / 18] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur), qf[f % 18],
-                                                                    s[f / 18], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        // online softmax in the exp2 domain (per head = per lane column)
-        const int row0 = j * kTile;
-        float tmax = -INFINITY;
+                for (int f = 0; f < kLookK; ++f) ring[f] = kload(f);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * n + 4 * G + i;
-                float x = s[n][i] * c2;
-                if constexpr (FP8) x *= sm.f8scale[r];
-                x = (row0 + r < n_valid) ? x : -INFINITY;
-                s[n][i] = x;
-                tmax = fmaxf(tmax, x);
-            }
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        float psum = 0.0f;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int n = 2 * m + hh;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float p = __builtin_amdgcn_exp2f(s[n][i] - m_use);
-                    psum += p;
-                    if constexpr (FP8) p *= sm.f8scale[16 * n + 4 * G + i];
-                    pb[m][4 * hh + i] = (__bf16)p;
+                for (int f = 0; f < 2 * kKSteps; ++f) {
+                    const uint4 cur = ring[f % kLookK];
+                    if (f + kLookK < 2 * kKSteps) ring[f % kLookK] = kload(f + kLookK);
+                    s[f & 1] = mfma32_bf16(__builtin_bit_cast(bf16x8, cur), qf[f >> 1], s[f & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-        }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < 32; ++dt) o[dt] *= alpha;
 
-        // O^T += V^T P^T; k-step m covers rows {32 m + 4 G + i} u {32 m + 16 + 4 G + i}.
-        // Same bounded look-ahead as above over the 64 (k-step, dim-tile) steps.
-        {
-            const uint8_t *vbase = tile + (4 * G + (i16 >> 2)) * kRowB + 4 * (i16 & 3) * 2;
-            auto vload = [&](int f, bf16x4 &lo, bf16x4 &hi) {
-                const uint8_t *p = vbase + (f / 32) * 32 * kRowB + 32 * (f % 32);
-                lo = lds_tr16(p);
-                hi = lds_tr16(p + 16 * kRowB);
-            };
-            bf16x4 rlo[kLook], rhi[kLook];
+            // softmax (exp2 domain) per head = per lane column; lanes l and l ^ 32 hold
+            // disjoint rows of the same head
+            const int row0 = j * kTile;
+            float tmax = -INFINITY;
 #pragma unroll
-            for (int f = 0; f < kLook; ++f) vload(f, rlo[f], rhi[f]);
+            for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-            for (int f = 0; f < 64; ++f) {
-                const bf16x4 lo = rlo[f % kLook], hi = rhi[f % kLook];
-                if (f + kLook < 64) vload(f + kLook, rlo[f % kLook], rhi[f % kLook]);
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[f % 32] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[f / 32], o[f % 32], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < 16; ++i) {
+                    const int r = tau(32 * hf + 8 * (i >> 2) + 4 * g + (i & 3));   // tile row
+                    float x = s[hf][i] * c2;
+                    if constexpr (FP8) x *= sm.f8scale[r];
+                    x = (row0 + r < n_valid) ? x : -INFINITY;
+                    s[hf][i] = x;
+                    tmax = fmaxf(tmax, x);
+                }
             }
+            tmax = fmaxf(tmax, swap_halves(tmax));
+            m_seen = fmaxf(m_seen, tmax);
+            if (m_ref == -INFINITY) m_ref = tmax;             // first tile of this head: nothing accumulated yet
+            if (__ballot(tmax > m_ref + kHeadroom) != 0) sm.restart = 1u;   // acted on after the next barrier
+            const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+            float psum = 0.0f;
+            bf16x8 pb[4];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float p = __builtin_amdgcn_exp2f(s[hf][i] - m_use);
+                    psum += p;
+                    if constexpr (FP8) p *= sm.f8scale[tau(32 * hf + 8 * (i >> 2) + 4 * g + (i & 3))];
+                    pb[2 * hf + (i >> 3)][i & 7] = (__bf16)p;
+                }
+            }
+            l_run += psum;
+
+            // O^T += V^T P^T: k-step kk covers rho 16 kk + {4 g + e} u {16 kk + 8 + 4 g + e},
+            // dim tile dt covers dims 32 dt .. +32.  Same bounded look-ahead as above.
+            {
+                const uint8_t *vb = tile + v_base;
+                auto vload = [&](int f, bf16x4 &lo, bf16x4 &hi) {
+                    const uint8_t *p = vb + (f >> 4) * 16 * kRowB + 64 * (f & 15);
+                    lo = lds_tr16(p);
+                    hi = lds_tr16(p + 2 * kRowB);
+                };
+                bf16x4 rlo[kLookV], rhi[kLookV];
+#pragma unroll
+                for (int f = 0; f < kLookV; ++f) vload(f, rlo[f], rhi[f]);
+#pragma unroll
+                for (int f = 0; f < 64; ++f) {
+                    const bf16x4 lo = rlo[f % kLookV], hi = rhi[f % kLookV];
+                    if (f + kLookV < 64) vload(f + kLookV, rlo[f % kLookV], rhi[f % kLookV]);
+                    const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    o[f & 15] = mfma32_bf16(a, pb[f >> 4], o[f & 15]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            return false;
+        };
+        uint8_t *const buf_a = FP8 ? f8_a : tile_a;
+        uint8_t *const buf_b = FP8 ? f8_b : tile_b;
+        if (n_tiles > 0) gather(0, buf_a);
+        for (int j = 0; j < n_tiles; j += 2) {
+            if (step(j, buf_a, buf_b)) break;
+            if (j + 1 < n_tiles && step(j + 1, buf_b, buf_a)) break;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        again = sm.restart != 0;
+        if (again) {
+            __syncthreads();                              // everyone has read the flag
+            if (tid == 0) sm.restart = 0;
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
+            l_run = 0.0f;
+            m_ref = m_seen;
         }
     }
 
-    // ---- finish: the four 16-lane groups hold disjoint key subsets of each head
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    // ---- finish: lanes l and l ^ 32 hold disjoint row subsets of each head
+    const float l_tot = l_run + swap_halves(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const float lse_v = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    const float m_fin = m_ref == -INFINITY ? 0.0f : m_ref;
+    const float lse_v = l_tot > 0.0f ? (m_fin + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
     if (!head_ok) return;
     if constexpr (!SPLIT) {
-        uint16_t *orow = out + ((int64_t)t * h + head) * kDv + 4 * G;
+        uint16_t *orow = out + ((int64_t)t * h + head) * kDv + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) {
-            bf16x4 v;
+        for (int dt = 0; dt < 16; ++dt) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[dt][e] * inv);
-            *reinterpret_cast<bf16x4 *>(orow + 16 * dt) = v;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                bf16x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[dt][4 * q4 + e] * inv);
+                *reinterpret_cast<bf16x4 *>(orow + 32 * dt + 8 * q4) = v;
+            }
         }
-        if (lse != nullptr && G == 0) lse[(int64_t)t * h + head] = lse_v;
+        if (lse != nullptr && g == 0) lse[(int64_t)t * h + head] = lse_v;
     } else {
-        float *orow = ws_o + (((int64_t)t * n_splits + split) * h + head) * kDv + 4 * G;
+        float *orow = ws_o + (((int64_t)t * n_splits + split) * h + head) * kDv + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt)
-            *reinterpret_cast<float4 *>(orow + 16 * dt) =
-                make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-        if (G == 0) ws_lse[((int64_t)t * n_splits + split) * h + head] = lse_v;
+        for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<float4 *>(orow + 32 * dt + 8 * q4) =
+                    make_float4(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv, o[dt][4 * q4 + 2] * inv,
+                                o[dt][4 * q4 + 3] * inv);
+        if (g == 0) ws_lse[((int64_t)t * n_splits + split) * h + head] = lse_v;
     }
 }
 
@@ -367,12 +452,12 @@ static void launch_mla_t(const MlaArgs &a, int n_splits, float *ws_o, float *ws_
 
 template <bool FP8, bool SPLIT>
 static void launch_mla_nw(const MlaArgs &a, int n_splits, float *ws_o, float *ws_lse, hipStream_t stream) {
-    const int nw = (a.h + 15) / 16;
+    const int nw = (a.h + 31) / 32;   // 32 heads per wave
     switch (nw) {
     case 1: launch_mla_t<1, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
     case 2: launch_mla_t<2, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
-    case 4: launch_mla_t<4, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
-    default: launch_mla_t<8, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
+    case 3: launch_mla_t<3, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
+    default: launch_mla_t<4, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
     }
 }
 
