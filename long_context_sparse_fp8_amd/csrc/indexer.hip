@@ -217,9 +217,16 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 }
 
 // ------------------------------------------------------------------ decode
-// Workgroup = one query x a range of key pages; the 4 waves take pages
-// round-robin and load B fragments straight from the cache (each key byte is
-// used by exactly one query, so there is nothing to share through LDS).
+constexpr int kWavePages = 16;                    // page slots per wave (4 waves: 64 pages per split)
+
+// Workgroup = one query x a range of at most 64 key pages; the 4 waves take
+// pages round-robin and load B fragments straight from the cache (each key
+// byte is used by exactly one query, so there is nothing to share through
+// LDS).  The scan is bound by HBM, so the kernel keeps as many bytes in flight
+// as its registers allow: the split's page-table entries are read once up front
+// (lane i holds page p_begin + i, broadcast with a lane read), so no key load
+// waits on a table load, and every wave keeps two pages in flight ahead of the
+// one it is scoring.
 template <int H_I, int D_I>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint8_t *__restrict__ q_fp8, const float *__restrict__ q_scale, const float *__restrict__ w, int64_t w_ld,
@@ -234,53 +241,67 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const int64_t max_page = (ld + kPage - 1) / kPage;
     if (n_pg > max_page) n_pg = max_page;
     const int64_t p_begin = (int64_t)blockIdx.y * pages_per_split;
-    const int64_t p_end = min(n_pg, p_begin + pages_per_split);
+    const int64_t p_end = min(n_pg, p_begin + pages_per_split);   // pages_per_split <= 4 kWavePages
     if (p_begin >= p_end) return;
+    if (n_pages <= 0) {                                  // no page can be read: every score is NaN
+        for (int64_t key = p_begin * kPage + threadIdx.x; key < min(p_end * kPage, min((int64_t)pos + 1, ld));
+             key += 256)
+            scores[(int64_t)t * ld + key] = __builtin_nanf("");
+        return;
+    }
 
+    // physical page of page p_begin + lane, -1 when absent or out of range
+    int32_t my_phys = -1;
+    {
+        const int32_t *pt_row = page_table + (int64_t)q_seq[t] * pt_ld;
+        const int64_t pp = p_begin + lane;
+        if (pp < p_end && pp < pt_ld) {
+            const int32_t v = pt_row[pp];
+            if (v >= 0 && v < n_pages) my_phys = v;
+        }
+    }
     QueryFrag<H_I, D_I> q;
     load_query<H_I, D_I>(q, q_fp8, w, w_ld, t, lane);
     const float qs = q_scale[t];
-    const int32_t *pt_row = page_table + (int64_t)q_seq[t] * pt_ld;
 
-    auto fetch = [&](int64_t p, i32x8 (&b)[2][S::KC], float &ksc) {
-        const int64_t phys = p < pt_ld ? (int64_t)pt_row[p] : -1;
-        const bool ok = phys >= 0 && phys < n_pages;
-        const uint8_t *base = key_cache + (ok ? phys : 0) * (kPage * D_I);
+    // Page slot m of this wave is page p_begin + wave + 4 m.  Every wave runs all
+    // kWavePages slots, fully unrolled and branch-free: a slot past the split
+    // loads a page of the split again and stores nothing.  With no loop back-edge
+    // the compiler can wait for exactly the page being scored while the next two
+    // stay in flight.
+    auto fetch = [&](int m, i32x8 (&b)[2][S::KC], float &ksc) {
+        const int64_t p = min(p_begin + wave + 4 * m, p_end - 1);
+        const int32_t phys0 = __builtin_amdgcn_readlane(my_phys, (int)(p - p_begin));
+        const int32_t phys = phys0 < 0 ? 0 : phys0;      // absent page: scores become NaN below
+        const uint8_t *base = key_cache + (int64_t)phys * (kPage * D_I);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int c = 0; c < S::KC; ++c) {
-                i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (ok) {
-                    const uint4 *src = reinterpret_cast<const uint4 *>(base + (32 * kt + (lane & 31)) * D_I +
-                                                                       g * S::HALF + 32 * c);
-                    const uint4 lo = src[0], hi = src[1];
-                    v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                }
-                b[kt][c] = v;
+                const uint4 *src = reinterpret_cast<const uint4 *>(base + (32 * kt + (lane & 31)) * D_I +
+                                                                   g * S::HALF + 32 * c);
+                const uint4 lo = src[0], hi = src[1];
+                b[kt][c] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             }
         }
-        ksc = ok ? key_scale[phys * kPage + lane] : __builtin_nanf("");
+        const float k = key_scale[(int64_t)phys * kPage + lane];
+        ksc = phys0 < 0 ? __builtin_nanf("") : k;
     };
-
-    i32x8 b[2][S::KC];
-    float ksc;
-    int64_t p = p_begin + wave;
-    if (p < p_end) fetch(p, b, ksc);
-    while (p < p_end) {
-        i32x8 bn[2][S::KC];
-        float kn = 0.0f;
-        const int64_t pn = p + 4;
-        if (pn < p_end) fetch(pn, bn, kn);
+    auto score = [&](int m, const i32x8 (&b)[2][S::KC], float ksc) {
+        const int64_t p = p_begin + wave + 4 * m;
         const float sc = page_scores<H_I, D_I>(q, b);
         const int64_t key = p * kPage + lane;
-        if (key <= pos && key < ld) scores[(int64_t)t * ld + key] = sc * (qs * ksc);
-        p = pn;
+        if (p < p_end && key <= pos && key < ld) scores[(int64_t)t * ld + key] = sc * (qs * ksc);
+    };
+
+    i32x8 bf[3][2][S::KC];
+    float kf[3];
+    fetch(0, bf[0], kf[0]);
+    fetch(1, bf[1], kf[1]);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int c = 0; c < S::KC; ++c) b[kt][c] = bn[kt][c];
-        ksc = kn;
+    for (int m = 0; m < kWavePages; ++m) {
+        if (m + 2 < kWavePages) fetch(m + 2, bf[(m + 2) % 3], kf[(m + 2) % 3]);
+        score(m, bf[m % 3], kf[m % 3]);
     }
 }
 
@@ -289,7 +310,7 @@ template <int H_I, int D_I>
 static hipError_t launch_indexer_t(const IndexerArgs &a, hipStream_t stream) {
     if (a.n_q <= kIndexerDecodeMaxQ) {
         // few queries: split each query's key range over workgroups
-        const int pps = 64;
+        const int pps = 4 * kWavePages;            // 64: one page-table entry per lane
         const int64_t splits = (a.pt_ld + pps - 1) / pps;
         dim3 grid((unsigned)a.n_q, (unsigned)(splits > 0 ? splits : 1));
         hipLaunchKernelGGL((indexer_decode_kernel<H_I, D_I>), grid, dim3(256), 0, stream, a.q_fp8, a.q_scale, a.w,

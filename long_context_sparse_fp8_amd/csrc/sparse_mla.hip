@@ -468,9 +468,12 @@ hipError_t launch_mla_prefill(const MlaArgs &a, hipStream_t stream) {
 }
 
 int mla_decode_auto_splits(int32_t n_q, int32_t k) {
-    // aim for >= 2 workgroups per CU over 256 CUs, at least 2 tiles per split
+    // One workgroup fills a CU (LDS-bound), so aim for about one workgroup per CU
+    // (256): every extra split re-reads the query's 128 x 576 q block and writes
+    // and re-reads a 128 x 512 fp32 partial, which at 64 queries costs more than
+    // the parallelism it adds (measured: 8 splits 120 us, 4 splits 85 us).
     int s = 1;
-    while (s < 32 && (int64_t)n_q * s < 512 && k / (2 * s) >= 2 * kTile) s *= 2;
+    while (s < 32 && (int64_t)n_q * s < 256 && k / (2 * s) >= 2 * kTile) s *= 2;
     return s;
 }
 
