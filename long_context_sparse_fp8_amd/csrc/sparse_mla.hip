@@ -12,52 +12,89 @@
 // gathered row is read from memory once per query and shared by all heads
 // through LDS.  Per 64-row tile:
 //   * the selected rows are gathered straight into LDS with
-//     global_load_lds_dwordx4 (no register staging), double-buffered, rows
-//     padded to 1168 bytes and the MFMA rows mapped to tile rows so that both
-//     the row reads and the transposed reads below are bank-conflict free;
+//     global_load_lds_dwordx4 (no register staging), double-buffered.  The tile
+//     is stored as eighteen 64-byte column blocks of 64 rows with the 16-byte
+//     chunks of every row XOR-swizzled, so that one copy instruction moves 16
+//     rows x 64 contiguous bytes, each lane keeps one source row for the whole
+//     tile (one slot lookup, then immediate offsets), and both MFMA operand
+//     reads below are bank-conflict free;
+//   * the copies of tile j + 1 and the softmax are spread between the MFMAs of
+//     tile j, so the matrix pipe never waits for address arithmetic or VALU work;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 gathered rows from LDS,
-//     B = the wave's 32 query heads held in VGPRs): each 16-byte LDS fragment
-//     feeds 32 heads, which halves LDS traffic per flop against 16-head tiles;
+//     B = the wave's 32 query heads held in VGPRs), in two 32-row halves: the
+//     softmax of half 0 runs under the MFMAs of half 1, that of half 1 under
+//     the first half of O^T += V^T P^T;
 //   * softmax per head (= per lane column) in the exp2 domain against a fixed
-//     reference: the head's maximum over its first tile.  Probabilities of later
-//     tiles may exceed 1 by up to 2^64 before the reference must move; that
+//     reference: the head's maximum over the first 32 rows.  Probabilities of
+//     later rows may exceed 1 by up to 2^64 before the reference must move; that
 //     range is exact in fp32 sums and bf16 probabilities, and the final division
 //     gives the same softmax as a running-max rescale.  A tile beyond it restarts
 //     the query with a raised reference instead of rescaling the accumulators,
 //     which keeps O^T in accumulation registers that VALU code never touches;
 //   * O^T += V^T P^T: P^T is the S^T accumulator re-packed to bf16 in place
-//     (its lane layout already is the B operand, with the k index permuted
-//     consistently on both operands), V^T comes from the same LDS tile through
-//     ds_read_b64_tr_b16 transposed reads.
+//     (its lane layout already is the B operand), V^T comes from the same LDS
+//     tile through ds_read_b64_tr_b16 transposed reads.
 // FP8 rows (E4M3 + per-row scale) are gathered as bytes, expanded to bf16 in
 // LDS exactly, and their scale is applied to the logits and to P in fp32.
+#include <utility>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 
 constexpr int kTile = 64;                         // gathered rows per tile
-constexpr int kRowB = kDk * 2 + 16;               // padded bf16 LDS row, bytes (1168)
-constexpr int kRowC = kRowB / 16;                 // 16-byte chunks per padded row (73)
-constexpr int kTileB = kTile * kRowB;             // 74752 bytes
-constexpr int kF8RowC = kDk / 16;                 // 16-byte chunks per FP8 row (36)
-constexpr int kF8TileB = kTile * kDk;             // 36864 bytes
+constexpr int kRowB = kDk * 2;                    // bf16 row bytes (1152)
+constexpr int kTileB = kTile * kRowB;             // 73728 bytes
+constexpr int kColB = kTile * 64;                 // one 64-byte column block of a tile (4096 bytes)
+constexpr int kF8TileB = kTile * kDk;             // 36864 bytes of staged FP8 codes
 constexpr int kMaxK = 2048;
 constexpr int kKSteps = kDk / 16;                 // 36 k-steps of 16 latent dims
+constexpr int kQK = 2 * kKSteps;                  // S^T MFMAs per tile per wave (two 32-row halves)
+constexpr int kPV = 4 * (kDv / 32);               // O^T MFMAs per tile per wave (4 k-steps x 16 dim tiles)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kHeadroom = 64.0f;                // log2 range allowed above a head's reference max
-constexpr int kLookK = 4;                         // K fragments in flight per wave
-constexpr int kLookV = 4;                         // V^T fragments in flight per wave
+// K / V^T fragments in flight per wave (register rings); the FP8 variant needs
+// registers for its row scales and keeps shorter rings.
+template <bool FP8> constexpr int kLookK = FP8 ? 2 : 4;
+template <bool FP8> constexpr int kLookV = FP8 ? 2 : 4;
+constexpr int kCopySpan = 136;                    // the next tile's copies are spread over this many MFMAs
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16-byte asynchronous global -> LDS copies: lane l of the wave writes
-// lds_base + 16 * l.
-__device__ __forceinline__ void g2lds16(const void *gsrc, lds_void *lds_base) {
-    __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+// 16-byte asynchronous global -> LDS copy: lane l of the wave reads gsrc + IMM
+// and writes lds_base + IMM + 16 l (the immediate offset advances both
+// addresses).  Written as inline assembly because the compiler models the
+// builtin form as an LDS access that may complete out of order, and then waits
+// for every outstanding LDS read (lgkmcnt(0)) after each copy, which drains the
+// register-ring prefetch of the MFMA operands.  The copy is tracked by vmcnt
+// only; its destination is read after an explicit s_waitcnt and a barrier.  It
+// has no register results.
+template <int IMM>
+__device__ __forceinline__ void g2lds16(const void *gsrc, uint32_t lds_base) {
+    static_assert(IMM >= 0 && IMM < 4096, "immediate offset");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+                 :
+                 : "v"(gsrc), "s"(lds_base), "i"(IMM)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ lds_void *to_lds(void *p) { return (lds_void *)(p); }
+// LDS byte address of a __shared__ object (wave-uniform)
+__device__ __forceinline__ uint32_t lds_addr(void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)to_lds(p));
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, so that
+// the body can use I where a constant expression is required.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p) {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -69,24 +106,34 @@ __device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8 &a, const bf16x8 &b, 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Tile rows are padded to 1168 bytes (73 16-byte chunks): 16 consecutive rows
-// then start on 16 distinct chunk columns modulo 16, so the row reads (16 lanes =
-// 16 rows x 16 bytes per cycle on gfx950's 64 banks) are conflict-free.  The
-// transposed reads fetch 4 rows x 32 bytes per 16-lane group; they are
-// conflict-free when those 4 rows are 4 apart.  So the MFMA row index rho (the
-// S^T accumulator row, and the k index of the PV product) maps to the tile row
-// tau(rho) that transposes the 4x4 blocks of every 16 rows:
-//   tau(16 B + 4 a + b) = 16 B + 4 b + a,
-// under which each transposed read's 4 consecutive k slots are tile rows 4
-// apart, and every fragment address is one per-lane base plus a constant.
-__device__ __forceinline__ int tau(int rho) { return (rho & ~15) | ((rho & 3) << 2) | ((rho >> 2) & 3); }
+// Workgroup barrier after this wave's LDS accesses and all but the newest N
+// vector-memory loads (in issue order) have completed.  The copies above are
+// invisible to the compiler's counter tracking, so every wait for them is written
+// out here; the empty asm statements keep memory accesses on their side.
+template <int N>
+__device__ __forceinline__ void barrier_after_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Tile layout: row r (0..63), 16-byte chunk c (0..71) of the bf16 row lives at
+//   (c / 4) * 4096 + 64 r + 16 ((c % 4) ^ swz(r)),  swz(r) = (r / 4) % 4.
+// The K fragment reads (16 lanes = 16 consecutive rows x one chunk per LDS cycle)
+// and the transposed V^T reads (32 lanes = 4 consecutive rows x 4 chunks x two
+// 8-byte halves) then touch 16 resp. 32 distinct bank groups.  A staged FP8
+// tile uses the same column blocks without the swizzle (9 blocks of 64 codes).
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int tile_off(int r, int c) { return (c >> 2) * kColB + 64 * r + 16 * ((c & 3) ^ swz(r)); }
 
 // Tile buffers live in separate __shared__ arrays, each named statically at every
 // use, so that the compiler can tell the asynchronous gather into one buffer from
 // the reads of the other and does not make the reads wait for the gather.
 template <int NW, bool FP8, bool SPLIT>
 struct MlaSmem {
-    float f8scale[FP8 ? kTile : 1];
+    float f8scale[FP8 ? kTile : 1];               // FP8 row scale
+    float f8logit[FP8 ? kTile : 1];               // FP8 row scale x sm_scale x log2(e)
     int32_t slots[kMaxK];
     uint32_t wcount[NW];
     int32_t n_valid;
@@ -99,8 +146,18 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     int64_t n_slots, const int32_t *__restrict__ kv_slot_table, int64_t kv_pt_ld, const int32_t *__restrict__ q_seq,
     const int32_t *__restrict__ idx, int32_t h, int32_t k, float sm_scale, uint16_t *__restrict__ out,
     float *__restrict__ lse, int32_t n_splits, float *__restrict__ ws_o, float *__restrict__ ws_lse) {
+    static_assert(NW == 1 || NW == 2 || NW == 4, "waves per workgroup");
     constexpr int NT = NW * 64;
     constexpr int R = (kMaxK + NT - 1) / NT;      // index entries per thread
+    // Copies per tile: one instruction moves 16 rows x 64 bytes (a 1 KB block of a
+    // column block); bf16 tiles have 18 column blocks, staged FP8 tiles 9, and 4
+    // row blocks each.  Wave w takes the row blocks w, w + NW, ..., so that a
+    // lane's source row is fixed for the tile.
+    constexpr int kCols = FP8 ? 9 : 18;
+    constexpr int kRBW = 4 / NW;                  // row blocks per wave
+    constexpr int kCopies = kCols * kRBW;         // copy instructions per wave per tile
+    constexpr int kCopyEvery = kCopySpan / kCopies > 0 ? kCopySpan / kCopies : 1;
+    static_assert(kCopies * kCopyEvery <= kQK + kPV, "copies must fit the MFMA stream");
     __shared__ __attribute__((aligned(16))) MlaSmem<NW, FP8, SPLIT> sm;
     // bf16 cache: tile_a / tile_b double buffer.  FP8 cache: codes staged in
     // f8_a / f8_b (double buffer), expanded into tile_a.
@@ -109,7 +166,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t f8_a[FP8 ? kF8TileB : 16];
     __shared__ __attribute__((aligned(16))) uint8_t f8_b[FP8 ? kF8TileB : 16];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;     // lane half, lane within the half
     const int i16 = lane & 15, hd = (lane >> 4) & 1;
     const int t = SPLIT ? (int)blockIdx.x / n_splits : (int)blockIdx.x;
@@ -120,16 +178,18 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const int head = 32 * wave + l32;
     const bool head_ok = head < h;
 
-    // ---- resolve the selected rows to cache slots, compacted in index order
+    // ---- resolve the selected rows to cache slots, compacted in index order:
+    // thread tid takes entries i_begin + R tid .. + R-1
     {
         const int32_t *idx_row = idx + (int64_t)t * k;
         const int32_t *st_row = kv_slot_table + (int64_t)q_seq[t] * kv_pt_ld;
         int32_t s[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int i = i_begin + tid + NT * r;
+            const int i = i_begin + R * tid + r;
             s[r] = i < i_end ? idx_row[i] : -1;
         }
+        int c = 0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             int32_t sl = -1;
@@ -138,28 +198,28 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                 if (v >= 0 && v < n_slots) sl = v;
             }
             s[r] = sl;
+            c += sl >= 0;
         }
-        int base = 0;
+        int x = c;                                // inclusive scan of the counts over the wave
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (i_begin + NT * r >= i_end) break;     // uniform
-            const bool ok = s[r] >= 0;
-            const uint64_t bal = __ballot(ok);
-            if (lane == 0) sm.wcount[wave] = (uint32_t)__builtin_popcountll(bal);
-            __syncthreads();
-            int before = base, tot = 0;
-#pragma unroll
-            for (int wv = 0; wv < NW; ++wv) {
-                const int c = (int)sm.wcount[wv];
-                if (wv < wave) before += c;
-                tot += c;
-            }
-            if (ok) sm.slots[before + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull))] = s[r];
-            base += tot;
-            __syncthreads();
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
         }
+        if (lane == 63) sm.wcount[wave] = (uint32_t)x;
+        __syncthreads();
+        int pos = x - c, tot = 0;
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) {
+            const int cw = (int)sm.wcount[wv];
+            if (wv < wave) pos += cw;
+            tot += cw;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (s[r] >= 0) sm.slots[pos++] = s[r];
         if (tid == 0) {
-            sm.n_valid = base;
+            sm.n_valid = tot;
             sm.restart = 0;
         }
     }
@@ -168,48 +228,49 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const int n_tiles = (n_valid + kTile - 1) / kTile;
 
     // ---- Q^T fragments of this wave's 32 heads (B operand): k-step ks holds
-    // latent dims 16 ks + 8 g .. +8 of head `head`
+    // latent dims 16 ks + 8 g .. +8 of head `head` (a missing head reads the
+    // last head's row; its results are never stored).  Loaded after the first
+    // tile's copies, so that the first tile only waits for those.
     bf16x8 qf[kKSteps];
-    {
-        const uint16_t *qrow = q + ((int64_t)t * h + (head_ok ? head : 0)) * kDk + 8 * g;
+    auto load_q = [&]() {
+        const uint16_t *qrow = q + ((int64_t)t * h + (head_ok ? head : h - 1)) * kDk + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (head_ok) v = *reinterpret_cast<const uint4 *>(qrow + 16 * ks);
-            qf[ks] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-
-    // ---- tile gather (asynchronous, straight to LDS, swizzled through the source addresses)
-    auto gather = [&](int j, uint8_t *dst) {
-        const int row0 = j * kTile;
-        const uint8_t *kvb = reinterpret_cast<const uint8_t *>(kv_cache);
-        if constexpr (!FP8) {
-            for (int ins = wave; ins < kRowC; ins += NW) {   // 73 wave-wide 1 KB copies
-                const int c = ins * 64 + lane;
-                const int r = c / kRowC, col = c - r * kRowC;
-                const int rr = row0 + r < n_valid ? row0 + r : 0;
-                const int64_t sl = sm.slots[rr];
-                // the pad chunk (col 72) takes a duplicate of chunk 71
-                g2lds16(kvb + sl * (kDk * 2) + (col < kRowC - 1 ? col : kRowC - 2) * 16, to_lds(dst + ins * 1024));
-            }
-        } else {
-            for (int ins = wave; ins < kF8RowC; ins += NW) {  // 36 wave-wide 1 KB copies
-                const int c = ins * 64 + lane;
-                const int r = c / kF8RowC, col = c - r * kF8RowC;
-                const int rr = row0 + r < n_valid ? row0 + r : 0;
-                const int64_t sl = sm.slots[rr];
-                g2lds16(kvb + sl * kDk + col * 16, to_lds(dst + ins * 1024));
-            }
-        }
+        for (int ks = 0; ks < kKSteps; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qrow + 16 * ks));
     };
-    // FP8: expand the staged codes of tile j into the bf16 tile (exact), fetch row scales
+
+    // ---- tile copies.  In row block b (16 rows) lane l takes row 16 b + l / 4 and
+    // the 16-byte piece l % 4 of each 64-byte column block, which for a bf16 tile
+    // holds chunk 4 col + ((l % 4) ^ swz(row)); swz(row) = (l / 16) % 4 for every
+    // row block.  So a copy is the lane's row address plus an immediate offset;
+    // the same immediate also advances the LDS address, which the LDS base
+    // argument compensates.
+    const float c2 = sm_scale * kLog2e;           // logits in log2 units: c2 * (q . k)
+    const uint8_t *kvb = reinterpret_cast<const uint8_t *>(kv_cache);
+    const int piece = FP8 ? (lane & 3) : ((lane & 3) ^ ((lane >> 4) & 3));
+    auto copy_src = [&](int j, int b) -> const uint8_t * {
+        const int r = 16 * (wave + NW * b) + (lane >> 2);
+        const int rr = j * kTile + r < n_valid ? j * kTile + r : 0;
+        const int64_t sl = sm.slots[rr];
+        return kvb + sl * (FP8 ? kDk : kRowB) + 16 * piece;
+    };
+    // copy instruction n (0 .. kCopies-1) of this wave: row block n / kCols, column block n % kCols
+    auto copy_one = [&](auto nc, const uint8_t *const *src, uint8_t *dst) {
+        constexpr int n = decltype(nc)::value;
+        constexpr int b = n / kCols, col = n % kCols;
+        const int rb = wave + NW * b;
+        g2lds16<64 * col>(src[b], lds_addr(dst) + col * (kColB - 64) + rb * 1024);
+    };
+    // FP8: expand the staged codes of tile j into the bf16 tile (exact) and fetch
+    // the row scales.  Staged block blk (1 KB) holds rows 16 (blk % 4) + l / 4,
+    // codes 64 (blk / 4) + 16 (l % 4) .. +16 in lane l's 16 bytes.
     auto expand = [&](int j, const uint8_t *src, uint8_t *dst_tile) {
         if constexpr (FP8) {
-            const int row0 = j * kTile;
-            for (int c = tid; c < kTile * kF8RowC; c += NT) {
-                const int r = c / kF8RowC, col = c - r * kF8RowC;
-                const uint4 v = *reinterpret_cast<const uint4 *>(&src[r * kDk + col * 16]);
+#pragma unroll
+            for (int n = 0; n < 36 / NW; ++n) {
+                const int blk = wave + NW * n;
+                const int r = 16 * (blk & 3) + (lane >> 2), c8 = 4 * (blk >> 2) + (lane & 3);
+                const uint4 v = *reinterpret_cast<const uint4 *>(&src[blk * 1024 + 16 * lane]);
                 const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
                 uint32_t o8[8];
 #pragma unroll
@@ -221,25 +282,33 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                     o8[2 * e] = __builtin_bit_cast(uint32_t, b0);
                     o8[2 * e + 1] = __builtin_bit_cast(uint32_t, b1);
                 }
-                uint4 *d = reinterpret_cast<uint4 *>(&dst_tile[r * kRowB + col * 32]);
-                d[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
-                d[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
+                *reinterpret_cast<uint4 *>(&dst_tile[tile_off(r, 2 * c8)]) = make_uint4(o8[0], o8[1], o8[2], o8[3]);
+                *reinterpret_cast<uint4 *>(&dst_tile[tile_off(r, 2 * c8 + 1)]) = make_uint4(o8[4], o8[5], o8[6], o8[7]);
             }
             if (tid < kTile) {
-                const int rr = row0 + tid < n_valid ? row0 + tid : 0;
-                sm.f8scale[tid] = kv_scale[sm.slots[rr]];
+                const int rr = j * kTile + tid < n_valid ? j * kTile + tid : 0;
+                const float sc = kv_scale[sm.slots[rr]];
+                sm.f8scale[tid] = sc;
+                sm.f8logit[tid] = sc * c2;
             }
         }
     };
 
-    // Per-lane LDS byte offsets within a tile.  K fragment (k-step ks, half hf): tile
-    // row tau(l32) + 32 hf, dims 16 ks + 8 g  -> k_base + 32 hf rows + 32 ks bytes.
-    // V^T fragment (k-step kk, dim tile dt): k slots 8 g + e (e < 4) are rho =
-    // 16 kk + 4 g + e (lo) and rho + 8 (hi), i.e. tile rows 16 kk + 4 e + g and
-    // 16 kk + 4 e + g + 2; lane i16 of a 16-lane group supplies row e = i16 / 4,
-    // dims 32 dt + 16 hd + 4 (i16 % 4)  -> v_base + 16 kk rows + 64 dt bytes (+2 rows).
-    const int k_base = tau(l32) * kRowB + 16 * g;
-    const int v_base = (4 * (i16 >> 2) + g) * kRowB + 32 * hd + 8 * (i16 & 3);
+    // Per-lane LDS byte offsets within a tile.
+    // K fragment (half hf, k-step ks): row 32 hf + l32, chunk 2 ks + g
+    //   -> (ks / 2) * 4096 + 2048 hf + k_off[ks % 2].
+    // V^T fragment (k-step kk, dim tile dt, lo / hi): lane i16 of a 16-lane group
+    // supplies row 16 kk + 8 hi + 4 g + i16 / 4 at dims 32 dt + 16 hd + 4 (i16 % 4),
+    // i.e. chunk 4 dt + 2 hd + (i16 / 2) % 2, half i16 % 2
+    //   -> dt * 4096 + 1024 kk + v_off[hi].
+    int k_off[2], v_off[2];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) k_off[qq] = 64 * l32 + 16 * ((2 * qq + g) ^ swz(l32));
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+        const int r = 8 * hi + 4 * g + (i16 >> 2), cq = 2 * hd + ((i16 >> 1) & 1);
+        v_off[hi] = 64 * r + 16 * (cq ^ swz(r)) + 8 * (i16 & 1);
+    }
 
     // O^T accumulators: o[dt][i] holds latent dim 32 dt + 8 (i / 4) + 4 g + i % 4 of head `head`
     f32x16 o[16];
@@ -247,126 +316,154 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
-    // Softmax reference: each head's maximum over its first tile.  Later tiles are
-    // exponentiated against it as long as their maximum stays within kHeadroom
-    // (log2 units) of it, which fp32 sums and bf16 probabilities hold exactly as
-    // the rescaled form would; a tile beyond that restarts the query with the
-    // larger reference, so the accumulators are never rescaled.
+    // Softmax reference: each head's maximum over the first 32 rows.  Later rows
+    // are exponentiated against it as long as their tile's maximum stays within
+    // kHeadroom (log2 units) of it, which fp32 sums and bf16 probabilities hold
+    // exactly as the rescaled form would; a tile beyond that restarts the query
+    // with the larger reference, so the accumulators are never rescaled.
     float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
-    const float c2 = sm_scale * kLog2e;
 
     // Attempts: the second and later ones only run after a tile exceeded its head's
     // reference by more than kHeadroom (practically never); they restart from tile
     // 0 with every reference raised to the largest maximum seen so far.
-    bool again = true;
+    bool again = true, first_attempt = true;
     while (again) {
-        // one tile: `cur` holds tile j (bf16 rows, or FP8 codes to expand), the gather
-        // of tile j + 1 goes to `nxt`; returns true when the query must restart
+        // one tile: `cur` holds tile j (bf16 rows, or FP8 codes to expand), the copies
+        // of tile j + 1 go to `nxt`; returns true when the query must restart
         auto step = [&](const int j, uint8_t *cur, uint8_t *nxt) -> bool {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();                              // tile j landed; everyone is done with tile j-1
+            // tile j landed (the first tile of a query may leave the q loads in
+            // flight); everyone is done with tile j - 1
+            if (first_attempt && j == 0) barrier_after_loads<kKSteps>();
+            else barrier_after_loads<0>();
             if (sm.restart != 0) return true;             // workgroup-uniform; nothing is in flight
-            if (j + 1 < n_tiles) gather(j + 1, nxt);
+            // copies of tile j + 1 (the last tile copies its own rows again, into the
+            // idle buffer, so that the MFMA stream below has no branches)
+            const int jn = j + 1 < n_tiles ? j + 1 : j;
+            const uint8_t *src[kRBW];
+#pragma unroll
+            for (int b = 0; b < kRBW; ++b) src[b] = copy_src(jn, b);
             const uint8_t *tile = cur;
             if constexpr (FP8) {
                 expand(j, cur, tile_a);
-                __syncthreads();
+                barrier_after_loads<kKSteps>();
                 tile = tile_a;
             }
+            const int lim = n_valid - j * kTile - 4 * g;  // element (hf, i) is a valid row iff 32 hf + 8 (i/4) + i%4 < lim
+            const bool partial = j * kTile + kTile > n_valid;
 
-            // S^T = K Q^T: s[hf] covers rho = 32 hf + 8 (i / 4) + 4 g + i % 4.  The 72
-            // (k-step, half) fragment loads run kLookK steps ahead of their MFMA in a
-            // register ring; the scheduling barriers keep that order.
-            f32x16 s[2];
+            // S^T = K Q^T in two halves of 32 rows (accumulator s covers rows
+            // 32 hf + 8 (i / 4) + 4 g + i % 4), each followed by its softmax; then
+            // O^T += V^T P^T.  K fragments run kLookK MFMAs ahead in a register
+            // ring, V^T fragments kLookV; the copies of the next tile are spread
+            // over all MFMAs.  Scheduling barriers keep that order.
+            f32x16 s;
+            float rmax = -INFINITY, psum = 0.0f;          // raw max of q.k (FP8: of the log2 logits), sum of p
+            uint32_t pw[4][4];                            // P^T as bf16 pairs: k-step kk, pair e of 4
+            auto kload = [&](int f) {
+                const int hf = f / kKSteps, ks = f % kKSteps;
+                return *reinterpret_cast<const uint4 *>(tile + (ks >> 1) * kColB + 2048 * hf + k_off[ks & 1]);
+            };
+            auto vload = [&](int f, bf16x4 &lo, bf16x4 &hi) {
+                const int kk = f >> 4, dt = f & 15;
+                const uint8_t *p = tile + dt * kColB + 1024 * kk;
+                lo = lds_tr16(p + v_off[0]);
+                hi = lds_tr16(p + v_off[1]);
+            };
+            // softmax of the half just finished: p = 2^(c2 q.k - m_ref) (FP8: times
+            // the row scale in both places), packed to bf16 pairs of the P^T operand
+            auto softmax_half = [&](int hf) {
+                if (first_attempt && j == 0 && hf == 0) {   // reference of every head: max over rows 0..31
+                    float mx = -INFINITY;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+                    for (int i = 0; i < 16; ++i) {
+                        float x = s[i] * (FP8 ? sm.f8logit[8 * (i >> 2) + 4 * g + (i & 3)] : c2);
+                        mx = fmaxf(mx, 8 * (i >> 2) + (i & 3) < lim ? x : -INFINITY);
+                    }
+                    m_ref = fmaxf(mx, swap_halves(mx));
+                }
+                // rows past the selection only occur in the last tile: a separate
+                // (uniform) path keeps the masking out of every other tile
+                auto body = [&](auto masked) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[hf][i] = 0.0f;
-            {
-                const uint8_t *kb = tile + k_base;
-                auto kload = [&](int f) {
-                    return *reinterpret_cast<const uint4 *>(kb + (f & 1) * 32 * kRowB + 32 * (f >> 1));
+                    for (int i = 0; i < 16; i += 2) {
+                        float p[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int ii = i + e, rl = 32 * hf + 8 * (ii >> 2) + (ii & 3);
+                            float x, v = s[ii];
+                            if constexpr (FP8) {
+                                v *= sm.f8logit[rl + 4 * g];
+                                x = v - m_ref;
+                            } else {
+                                x = fmaf(v, c2, -m_ref);
+                            }
+                            if constexpr (decltype(masked)::value) {
+                                if (!(rl < lim)) { x = -INFINITY; v = -INFINITY; }
+                            }
+                            rmax = fmaxf(rmax, v);
+                            p[e] = __builtin_amdgcn_exp2f(x);
+                            psum += p[e];
+                            if constexpr (FP8) p[e] *= sm.f8scale[rl + 4 * g];
+                        }
+                        const bf16x2 pk = {(__bf16)p[0], (__bf16)p[1]};
+                        pw[2 * hf + (i >> 3)][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+                    }
                 };
-                uint4 ring[kLookK];
+                if (partial) body(std::true_type{});
+                else body(std::false_type{});
+            };
+            uint4 kr[kLookK<FP8>];
+            bf16x4 vlo[kLookV<FP8>], vhi[kLookV<FP8>];
 #pragma unroll
-                for (int f = 0; f < kLookK; ++f) ring[f] = kload(f);
-#pragma unroll
-                for (int f = 0; f < 2 * kKSteps; ++f) {
-                    const uint4 cur = ring[f % kLookK];
-                    if (f + kLookK < 2 * kKSteps) ring[f % kLookK] = kload(f + kLookK);
-                    s[f & 1] = mfma32_bf16(__builtin_bit_cast(bf16x8, cur), qf[f >> 1], s[f & 1]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-
-            // softmax (exp2 domain) per head = per lane column; lanes l and l ^ 32 hold
-            // disjoint rows of the same head
-            const int row0 = j * kTile;
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = tau(32 * hf + 8 * (i >> 2) + 4 * g + (i & 3));   // tile row
-                    float x = s[hf][i] * c2;
-                    if constexpr (FP8) x *= sm.f8scale[r];
-                    x = (row0 + r < n_valid) ? x : -INFINITY;
-                    s[hf][i] = x;
-                    tmax = fmaxf(tmax, x);
-                }
-            }
+            for (int f = 0; f < kLookK<FP8>; ++f) kr[f] = kload(f);
+            static_for<kQK>([&](auto fc) {
+                constexpr int f = decltype(fc)::value;
+                constexpr int ks = f % kKSteps;
+                if constexpr (f == kKSteps) softmax_half(0);
+                const uint4 kc = kr[f % kLookK<FP8>];
+                if constexpr (f + kLookK<FP8> < kQK) kr[f % kLookK<FP8>] = kload(f + kLookK<FP8>);
+                else if constexpr (f + kLookK<FP8> - kQK < kLookV<FP8>)
+                    vload(f + kLookK<FP8> - kQK, vlo[f + kLookK<FP8> - kQK], vhi[f + kLookK<FP8> - kQK]);
+                s = mfma32_bf16(__builtin_bit_cast(bf16x8, kc), qf[ks], ks == 0 ? f32x16{} : s);
+                if constexpr (f % kCopyEvery == 0 && f / kCopyEvery < kCopies)
+                    copy_one(std::integral_constant<int, f / kCopyEvery>{}, src, nxt);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            softmax_half(1);
+            static_for<kPV>([&](auto fc) {
+                constexpr int f = decltype(fc)::value;
+                if constexpr ((f + kQK) % kCopyEvery == 0 && (f + kQK) / kCopyEvery < kCopies)
+                    copy_one(std::integral_constant<int, (f + kQK) / kCopyEvery>{}, src, nxt);
+                const bf16x4 lo = vlo[f % kLookV<FP8>], hi = vhi[f % kLookV<FP8>];
+                if constexpr (f + kLookV<FP8> < kPV) vload(f + kLookV<FP8>, vlo[f % kLookV<FP8>], vhi[f % kLookV<FP8>]);
+                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const uint4 bw = make_uint4(pw[f >> 4][0], pw[f >> 4][1], pw[f >> 4][2], pw[f >> 4][3]);
+                o[f & 15] = mfma32_bf16(a, __builtin_bit_cast(bf16x8, bw), o[f & 15]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            float tmax = FP8 ? rmax : rmax * c2;          // c2 > 0: the max of the log2 logits
             tmax = fmaxf(tmax, swap_halves(tmax));
             m_seen = fmaxf(m_seen, tmax);
-            if (m_ref == -INFINITY) m_ref = tmax;             // first tile of this head: nothing accumulated yet
             if (__ballot(tmax > m_ref + kHeadroom) != 0) sm.restart = 1u;   // acted on after the next barrier
-            const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
-            float psum = 0.0f;
-            bf16x8 pb[4];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float p = __builtin_amdgcn_exp2f(s[hf][i] - m_use);
-                    psum += p;
-                    if constexpr (FP8) p *= sm.f8scale[tau(32 * hf + 8 * (i >> 2) + 4 * g + (i & 3))];
-                    pb[2 * hf + (i >> 3)][i & 7] = (__bf16)p;
-                }
-            }
             l_run += psum;
-
-            // O^T += V^T P^T: k-step kk covers rho 16 kk + {4 g + e} u {16 kk + 8 + 4 g + e},
-            // dim tile dt covers dims 32 dt .. +32.  Same bounded look-ahead as above.
-            {
-                const uint8_t *vb = tile + v_base;
-                auto vload = [&](int f, bf16x4 &lo, bf16x4 &hi) {
-                    const uint8_t *p = vb + (f >> 4) * 16 * kRowB + 64 * (f & 15);
-                    lo = lds_tr16(p);
-                    hi = lds_tr16(p + 2 * kRowB);
-                };
-                bf16x4 rlo[kLookV], rhi[kLookV];
-#pragma unroll
-                for (int f = 0; f < kLookV; ++f) vload(f, rlo[f], rhi[f]);
-#pragma unroll
-                for (int f = 0; f < 64; ++f) {
-                    const bf16x4 lo = rlo[f % kLookV], hi = rhi[f % kLookV];
-                    if (f + kLookV < 64) vload(f + kLookV, rlo[f % kLookV], rhi[f % kLookV]);
-                    const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    o[f & 15] = mfma32_bf16(a, pb[f >> 4], o[f & 15]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
             return false;
         };
         uint8_t *const buf_a = FP8 ? f8_a : tile_a;
         uint8_t *const buf_b = FP8 ? f8_b : tile_b;
-        if (n_tiles > 0) gather(0, buf_a);
+        if (n_tiles > 0) {
+            const uint8_t *src[kRBW];
+#pragma unroll
+            for (int b = 0; b < kRBW; ++b) src[b] = copy_src(0, b);
+            static_for<kCopies>([&](auto nc) { copy_one(nc, src, buf_a); });
+        }
+        if (first_attempt) load_q();
         for (int j = 0; j < n_tiles; j += 2) {
             if (step(j, buf_a, buf_b)) break;
             if (j + 1 < n_tiles && step(j + 1, buf_b, buf_a)) break;
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        barrier_after_loads<0>();
         again = sm.restart != 0;
+        first_attempt = false;
         if (again) {
             __syncthreads();                              // everyone has read the flag
             if (tid == 0) sm.restart = 0;
@@ -456,8 +553,7 @@ static void launch_mla_nw(const MlaArgs &a, int n_splits, float *ws_o, float *ws
     switch (nw) {
     case 1: launch_mla_t<1, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
     case 2: launch_mla_t<2, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
-    case 3: launch_mla_t<3, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
-    default: launch_mla_t<4, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;
+    default: launch_mla_t<4, FP8, SPLIT>(a, n_splits, ws_o, ws_lse, stream); break;   // 3 x 32 heads run as 4
     }
 }
 
