@@ -183,20 +183,21 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     {
         const int32_t *idx_row = idx + (int64_t)t * k;
         const int32_t *st_row = kv_slot_table + (int64_t)q_seq[t] * kv_pt_ld;
+        // loads are issued unconditionally (clamped addresses, results selected
+        // afterwards), so that each round trip is waited for once
         int32_t s[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = i_begin + R * tid + r;
-            s[r] = i < i_end ? idx_row[i] : -1;
+            const int32_t v = idx_row[min(max(i, 0), k - 1)];
+            s[r] = i < i_end ? v : -1;
         }
         int c = 0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            int32_t sl = -1;
-            if (s[r] >= 0 && s[r] < kv_pt_ld) {
-                const int32_t v = st_row[s[r]];
-                if (v >= 0 && v < n_slots) sl = v;
-            }
+            const bool in_table = s[r] >= 0 && s[r] < kv_pt_ld;
+            const int32_t v = st_row[in_table ? s[r] : 0];
+            const int32_t sl = in_table && v >= 0 && v < n_slots ? v : -1;
             s[r] = sl;
             c += sl >= 0;
         }
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     // ---- Q^T fragments of this wave's 32 heads (B operand): k-step ks holds
     // latent dims 16 ks + 8 g .. +8 of head `head` (a missing head reads the
     // last head's row; its results are never stored).  Loaded after the first
-    // tile's copies, so that the first tile only waits for those.
+    // tile's copies are issued.
     bf16x8 qf[kKSteps];
     auto load_q = [&]() {
         const uint16_t *qrow = q + ((int64_t)t * h + (head_ok ? head : h - 1)) * kDk + 8 * g;
@@ -331,10 +332,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
         // one tile: `cur` holds tile j (bf16 rows, or FP8 codes to expand), the copies
         // of tile j + 1 go to `nxt`; returns true when the query must restart
         auto step = [&](const int j, uint8_t *cur, uint8_t *nxt) -> bool {
-            // tile j landed (the first tile of a query may leave the q loads in
-            // flight); everyone is done with tile j - 1
-            if (first_attempt && j == 0) barrier_after_loads<kKSteps>();
-            else barrier_after_loads<0>();
+            barrier_after_loads<0>();                     // tile j landed; everyone is done with tile j - 1
             if (sm.restart != 0) return true;             // workgroup-uniform; nothing is in flight
             // copies of tile j + 1 (the last tile copies its own rows again, into the
             // idle buffer, so that the MFMA stream below has no branches)
@@ -456,7 +454,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
             for (int b = 0; b < kRBW; ++b) src[b] = copy_src(0, b);
             static_for<kCopies>([&](auto nc) { copy_one(nc, src, buf_a); });
         }
-        if (first_attempt) load_q();
+        if (first_attempt) {
+            load_q();
+            // q is complete before the tile loop, so that the compiler's own counter
+            // tracking does not wait for it (and for the copies behind it) inside
+            __builtin_amdgcn_s_waitcnt(0);
+        }
         for (int j = 0; j < n_tiles; j += 2) {
             if (step(j, buf_a, buf_b)) break;
             if (j + 1 < n_tiles && step(j + 1, buf_b, buf_a)) break;
