@@ -56,7 +56,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kHeadroom = 64.0f;                // log2 range allowed above a head's reference max
 // K / V^T fragments in flight per wave (register rings); the FP8 variant needs
 // registers for its row scales and keeps shorter rings.
-template <bool FP8> constexpr int kLookK = FP8 ? 2 : 4;
+template <bool FP8> constexpr int kLookK = 4;
 template <bool FP8> constexpr int kLookV = FP8 ? 2 : 4;
 constexpr int kCopySpan = 136;                    // the next tile's copies are spread over this many MFMAs
 
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     // codes 64 (blk / 4) + 16 (l % 4) .. +16 in lane l's 16 bytes.
     auto expand = [&](int j, const uint8_t *src, uint8_t *dst_tile) {
         if constexpr (FP8) {
-#pragma unroll
+#pragma unroll 1
             for (int n = 0; n < 36 / NW; ++n) {
                 const int blk = wave + NW * n;
                 const int r = 16 * (blk & 3) + (lane >> 2), c8 = 4 * (blk >> 2) + (lane & 3);
