@@ -145,8 +145,11 @@ dsa_status dsa_indexer_scores(const uint8_t *q_fp8, const float *q_scale, const 
  * Stage 2: top-k selection
  * ------------------------------------------------------------------------ */
 
-/* Bytes of workspace dsa_topk needs for these sizes (0 = none; ws may then
- * be NULL). */
+/* Bytes of workspace with which dsa_topk splits each of few long rows over
+ * several workgroups (each keeps the k best of its part of the row, a second
+ * pass selects among the survivors; the result is identical).  0 when these
+ * sizes are not split.  The workspace is optional: with ws = NULL or fewer
+ * bytes every row is selected by one workgroup. */
 size_t dsa_topk_workspace_size(int32_t n_q, int64_t max_len, int32_t k);
 
 /* Per row t, over candidates s in [0, q_pos[t]] of scores[t, :]: keep the
@@ -161,6 +164,8 @@ size_t dsa_topk_workspace_size(int32_t n_q, int64_t max_len, int32_t k);
  *   scores [n_q, scores_ld] fp32 (q_pos[t] < scores_ld is the caller's contract;
  *          columns at or beyond scores_ld are never read)
  *   idx    [n_q, k] int32
+ *   ws     optional device workspace (see dsa_topk_workspace_size), any
+ *          alignment; owned by the caller and not read back by it
  * Supported: 1 <= k <= 2048, scores_ld <= DSA_MAX_TOPK_ROW (DSA_ERR_UNSUPPORTED
  * otherwise). */
 dsa_status dsa_topk(const float *scores, int64_t scores_ld, const int32_t *q_pos, int32_t n_q, int32_t k,

@@ -126,27 +126,22 @@ DSA_EXPORT dsa_status dsa_indexer_scores(const uint8_t *q_fp8, const float *q_sc
 }
 
 DSA_EXPORT size_t dsa_topk_workspace_size(int32_t n_q, int64_t max_len, int32_t k) {
-    (void)n_q;
-    (void)max_len;
-    (void)k;
-    return 0;
+    if (n_q <= 0 || max_len <= 0 || k < 1 || k > DSA_MAX_TOPK || max_len > DSA_MAX_TOPK_ROW) return 0;
+    return dsa::topk_ws_bytes(n_q, max_len, k);
 }
 
 DSA_EXPORT dsa_status dsa_topk(const float *scores, int64_t scores_ld, const int32_t *q_pos, int32_t n_q, int32_t k,
                                int32_t *idx, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
     REQUIRE(n_q >= 0, DSA_ERR_BAD_SHAPE, "dsa_topk: n_q = %d < 0", n_q);
     REQUIRE(k >= 1 && k <= DSA_MAX_TOPK, DSA_ERR_UNSUPPORTED, "dsa_topk: k = %d not in [1, %d]", k, DSA_MAX_TOPK);
     REQUIRE(scores_ld >= 1, DSA_ERR_BAD_SHAPE, "dsa_topk: scores_ld = %lld < 1", (long long)scores_ld);
     REQUIRE(scores_ld <= DSA_MAX_TOPK_ROW, DSA_ERR_UNSUPPORTED, "dsa_topk: scores_ld = %lld > %d",
             (long long)scores_ld, DSA_MAX_TOPK_ROW);
-    REQUIRE(ws_bytes >= dsa_topk_workspace_size(n_q, scores_ld, k), DSA_ERR_WORKSPACE_TOO_SMALL,
-            "dsa_topk: workspace too small");
     if (n_q == 0) return DSA_OK;
     REQUIRE_PTR(scores);
     REQUIRE_PTR(q_pos);
     REQUIRE_PTR(idx);
-    hipError_t e = dsa::launch_topk(scores, scores_ld, q_pos, n_q, k, idx, (hipStream_t)stream);
+    hipError_t e = dsa::launch_topk(scores, scores_ld, q_pos, n_q, k, idx, ws, ws ? ws_bytes : 0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "dsa_topk launch");
     return DSA_OK;
 }

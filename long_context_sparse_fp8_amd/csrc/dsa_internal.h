@@ -53,7 +53,10 @@ hipError_t launch_kv_store(const uint16_t *kv, const int64_t *slot, int32_t n, i
                            int64_t n_slots, hipStream_t stream);
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream);
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k, int32_t *idx,
-                       hipStream_t stream);
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+// Workspace that lets dsa_topk split few long rows over several workgroups
+// (0 when it does not split at these sizes).
+size_t topk_ws_bytes(int32_t n_q, int64_t ld, int32_t k);
 hipError_t launch_mla_prefill(const MlaArgs &a, hipStream_t stream);
 hipError_t launch_mla_decode(const MlaArgs &a, int n_splits, void *ws, hipStream_t stream);
 int mla_decode_auto_splits(int32_t n_q, int32_t k);

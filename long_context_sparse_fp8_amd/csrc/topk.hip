@@ -28,6 +28,16 @@
 // row here); longer rows are streamed chunk by chunk for each sweep (they are
 // few: one per decode sequence, and the re-reads hit L2).  Everything is
 // integer, so the selection is exact for the given scores.
+//
+// Few long rows (decode: one row of up to 128K scores per sequence) would leave
+// most of the chip idle with one workgroup per row.  With a workspace, such a
+// row is cut into P parts of at least 2k scores: each part keeps its own k best
+// (PART launch, one workgroup per part), and a second selection over the P x k
+// survivors, laid out in index order, picks the final k (MERGE launch).  Every
+// element of the row's top-k is in its part's top-k under the same ranking, and
+// ties between survivors still fall to the lower original index, so the result
+// is the same as the one-workgroup selection.
+#include <algorithm>
 #include <type_traits>
 
 #include "dsa_device.h"
@@ -147,26 +157,59 @@ __device__ __noinline__ void pick_digit(TopkSmem &sm, int nb, uint32_t rem, bool
     }
 }
 
+enum TopkMode { kWholeRow = 0, kPart = 1, kMerge = 2 };
+
+// Parts of a row of n scores when splitting into at most `parts` (each part
+// holds at least 2k scores).
+__device__ __forceinline__ int topk_row_parts(int n, int k, int parts) {
+    return max(1, min(parts, n / (2 * k)));
+}
+
 // C > 0: rows of at most C chunks, keys held in registers.  C == 0: chunks are
-// streamed from memory in every sweep.
-template <int C, bool VEC>
+// streamed from memory in every sweep.  MODE kWholeRow: row t of scores.
+// kPart: part blockIdx.y of row t; a row of one part writes the final result,
+// otherwise the part's k survivors (original index and score) go to the
+// workspace at [t, part].  kMerge: the survivors of row t (rows of one part are
+// done already).
+template <int C, bool VEC, int MODE>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
                                                              const int32_t *__restrict__ q_pos, int32_t k,
-                                                             int32_t *__restrict__ idx) {
+                                                             int32_t *__restrict__ idx, int32_t parts,
+                                                             float *__restrict__ ws_score,
+                                                             int32_t *__restrict__ ws_idx) {
     __shared__ __attribute__((aligned(16))) TopkSmem sm;
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int64_t n64 = (int64_t)q_pos[t] + 1;
     if (n64 > ld) n64 = ld;
     if (n64 < 0) n64 = 0;
-    const int n = (int)n64;   // n <= ld <= kTopkMaxRow (checked by the API)
+    int n = (int)n64;   // n <= ld <= kTopkMaxRow (checked by the API)
     int32_t *out = idx + (int64_t)t * k;
+    const float *row = scores + (int64_t)t * ld;
+    int base = 0, n_parts = 1;
+    if constexpr (MODE == kPart) {
+        n_parts = topk_row_parts(n, k, parts);
+        const int p = blockIdx.y;
+        if (p >= n_parts) return;
+        // parts of whole 4-score groups (aligned loads), the last one ending at n:
+        // at most 4 ceil(ceil(n / 4) / n_parts) scores each
+        const int64_t quads = (n + 3) / 4;
+        const int b0 = (int)(4 * ((int64_t)p * quads / n_parts));
+        const int b1 = p + 1 == n_parts ? n : (int)(4 * ((int64_t)(p + 1) * quads / n_parts));
+        base = b0;
+        row += b0;
+        n = b1 - b0;
+    } else if constexpr (MODE == kMerge) {
+        n_parts = topk_row_parts(n, k, parts);
+        if (n_parts == 1) return;
+        row = ws_score + (int64_t)t * parts * k;
+        n = n_parts * k;
+    }
 
-    if (n <= k) {   // every candidate is kept
+    if (n <= k) {   // every candidate is kept (a whole row, or a row of one part)
         for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
         return;
     }
-    const float *row = scores + (int64_t)t * ld;
     const int nc = (n + kChunk - 1) / kChunk;   // chunks of this row (uniform)
 
     uint32_t reg[C > 0 ? C : 1][4];
@@ -379,26 +422,75 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
         }
     }
     __syncthreads();
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = sm.stage[i];
+    if (MODE == kWholeRow || (MODE == kPart && n_parts == 1)) {
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = sm.stage[i];
+    } else if (MODE == kPart) {
+        const int64_t o = ((int64_t)t * parts + blockIdx.y) * k;
+        for (int i = tid; i < k; i += kTopkThreads) {
+            const int pos = sm.stage[i];
+            ws_idx[o + i] = base + pos;
+            ws_score[o + i] = row[pos];
+        }
+    } else {
+        const int32_t *map = ws_idx + (int64_t)t * parts * k;
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = map[sm.stage[i]];
+    }
+}
+
+int topk_parts(int32_t n_q, int64_t ld, int32_t k) {
+    // split only when the rows alone cannot fill the chip: about one part per
+    // CU of a 256-CU device (one round of workgroups measured faster than two
+    // rounds of smaller parts), parts of at least 4k scores on average
+    if (n_q > 128) return 1;
+    int p = 8;
+    while (p > 1 && ((int64_t)n_q * p > 256 || ld / p < 4 * (int64_t)k)) p >>= 1;
+    return p;
+}
+
+size_t topk_ws_bytes(int32_t n_q, int64_t ld, int32_t k) {
+    const int p = topk_parts(n_q, ld, k);
+    return p > 1 ? (size_t)n_q * p * k * (sizeof(float) + sizeof(int32_t)) + 256 : 0;
+}
+
+// Whole rows of up to `len` scores, VEC when row starts are 16-byte aligned.
+template <int MODE>
+static void launch_rows(dim3 grid, int64_t len, bool vec, const float *scores, int64_t ld, const int32_t *q_pos,
+                        int32_t k, int32_t *idx, int parts, float *ws_score, int32_t *ws_idx, hipStream_t stream) {
+    const dim3 block(kTopkThreads);
+#define DSA_TOPK_GO(C, V)                                                                                        \
+    hipLaunchKernelGGL((topk_kernel<C, V, MODE>), grid, block, 0, stream, scores, ld, q_pos, k, idx, parts, ws_score, \
+                       ws_idx)
+    if (vec) {
+        if (len <= 4 * kChunk) DSA_TOPK_GO(4, true);
+        else if (len <= 8 * kChunk) DSA_TOPK_GO(8, true);
+        else DSA_TOPK_GO(0, true);
+    } else {
+        if (len <= 8 * kChunk) DSA_TOPK_GO(8, false);
+        else DSA_TOPK_GO(0, false);
+    }
+#undef DSA_TOPK_GO
 }
 
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k, int32_t *idx,
-                       hipStream_t stream) {
-    const dim3 grid((unsigned)n_q), block(kTopkThreads);
+                       void *ws, size_t ws_bytes, hipStream_t stream) {
     // scores is 16-byte aligned (checked by the API), so rows are when ld % 4 == 0
-    if ((ld & 3) == 0) {
-        if (ld <= 4 * kChunk)
-            hipLaunchKernelGGL((topk_kernel<4, true>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
-        else if (ld <= 8 * kChunk)
-            hipLaunchKernelGGL((topk_kernel<8, true>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
-        else
-            hipLaunchKernelGGL((topk_kernel<0, true>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
-    } else {
-        if (ld <= 8 * kChunk)
-            hipLaunchKernelGGL((topk_kernel<8, false>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
-        else
-            hipLaunchKernelGGL((topk_kernel<0, false>), grid, block, 0, stream, scores, ld, q_pos, k, idx);
+    const bool vec = (ld & 3) == 0;
+    const int parts = topk_parts(n_q, ld, k);
+    if (parts == 1 || ws == nullptr || ws_bytes < topk_ws_bytes(n_q, ld, k)) {
+        launch_rows<kWholeRow>(dim3((unsigned)n_q), ld, vec, scores, ld, q_pos, k, idx, 1, nullptr, nullptr, stream);
+        return hipGetLastError();
     }
+    float *ws_score = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+    int32_t *ws_idx = reinterpret_cast<int32_t *>(ws_score + (size_t)n_q * parts * k);
+    // longest part: 4 ceil(ceil(ld / 4) / parts) scores, or about 4k in a row of
+    // fewer parts (a row of n scores has n / 2k of them)
+    const int64_t part_len = std::max<int64_t>(4 * (((ld + 3) / 4 + parts - 1) / parts), 4 * (int64_t)k + 4);
+    launch_rows<kPart>(dim3((unsigned)n_q, (unsigned)parts), part_len, vec, scores, ld, q_pos, k, idx, parts, ws_score,
+                       ws_idx, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_rows<kMerge>(dim3((unsigned)n_q), (int64_t)parts * k, ((int64_t)parts * k) % 4 == 0, scores, ld, q_pos, k,
+                        idx, parts, ws_score, ws_idx, stream);
     return hipGetLastError();
 }
 

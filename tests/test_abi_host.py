@@ -80,6 +80,10 @@ def test_topk_validation(L):
     assert L.dsa_topk(None, 100, A, 4, 16, A, None, 0, None) == 1
     assert L.dsa_topk(A, 100, A, 4, 16, MIS, None, 0, None) == 4
     assert L.dsa_topk_workspace_size(4, 100, 16) == 0
+    # few long rows split over workgroups: survivors (score + index) per part
+    assert L.dsa_topk_workspace_size(64, 131072, 2048) == 64 * 4 * 2048 * 8 + 256
+    assert L.dsa_topk_workspace_size(16, 131072, 2048) == 16 * 8 * 2048 * 8 + 256
+    assert L.dsa_topk_workspace_size(300, 131072, 2048) == 0
 
 
 def test_mla_validation(L):

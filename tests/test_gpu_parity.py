@@ -144,7 +144,8 @@ def test_indexer_shared_weights_and_columns_untouched():
 
 
 # ------------------------------------------------------------------ top-k
-@pytest.mark.parametrize("case", ["normal", "ties", "zeros", "short_rows", "wide", "odd_ld", "mid"])
+@pytest.mark.parametrize("case", ["normal", "ties", "zeros", "short_rows", "wide", "odd_ld", "mid",
+                                  "split_ties", "split_mixed"])
 def test_topk_bitexact_from_identical_scores(case):
     say(f"[topk] {case}")
     rng = np.random.default_rng(sum(map(ord, case)))
@@ -155,8 +156,10 @@ def test_topk_bitexact_from_identical_scores(case):
         n_q, ld, k = 50, 20001, 2048
     if case == "mid":               # register-resident rows of the 16K..32K variant
         n_q, ld, k = 64, 32768, 1000
+    if case in ("split_ties", "split_mixed"):   # few long rows: split over workgroups
+        n_q, ld, k = 64, 40000, 333 if case == "split_ties" else 2048
     s = rng.standard_normal((n_q, ld)).astype(np.float32)
-    if case == "ties":
+    if case in ("ties", "split_ties"):
         s = np.round(s * 2) / 2
     if case == "zeros":
         s[:, ::2] = 0.0
@@ -165,6 +168,9 @@ def test_topk_bitexact_from_identical_scores(case):
     pos[:4] = [0, k - 1, k, ld - 1]
     if case == "short_rows":
         pos = rng.integers(0, 2 * k, size=n_q).astype(np.int32)
+    if case == "split_mixed":       # one part, a few parts, and lengths at the part-count steps
+        pos[4:20] = [2 * k - 1, 2 * k, 4 * k - 1, 4 * k, 4 * k + 1, 6 * k + 3, 8 * k - 2, 8 * k, 16 * k - 1, 16 * k,
+                     16 * k + 5, 17 * k, 3 * k + 7, 5 * k - 3, 12345, 39999 - 1]
     if case == "ties":
         k = 333
     sd = torch.from_numpy(s).to(DEV)
@@ -174,6 +180,12 @@ def test_topk_bitexact_from_identical_scores(case):
     torch.cuda.synchronize()
     ref = oracle.topk(s, pos, k, n_threads=oracle_threads())
     np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+    if dsa.topk_workspace_size(n_q, ld, k) > 0:
+        # the same call without a workspace selects every row in one workgroup
+        idx1 = torch.full((n_q, k), -7, dtype=torch.int32, device=DEV)
+        assert dsa.lib().dsa_topk(sd.data_ptr(), ld, pd.data_ptr(), n_q, k, idx1.data_ptr(), None, 0, None) == 0
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx1.cpu().numpy(), ref)
 
 
 def test_topk_k_one_and_all_equal():
