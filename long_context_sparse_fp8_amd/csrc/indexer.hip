@@ -218,22 +218,34 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 
 // ------------------------------------------------------------------ decode
 constexpr int kWavePages = 16;                    // page slots per wave (4 waves: 64 pages per split)
+constexpr int kDecDepth = 1;                      // pages per wave in flight while one is scored
+
+// max(x, 0) on the bit pattern: one integer max, where the float max of an
+// MFMA result first has to quiet a possible signalling NaN.  Equal to the
+// float max for every number.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Workgroup = one query x a range of at most 64 key pages; the 4 waves take
 // pages round-robin and load B fragments straight from the cache (each key
 // byte is used by exactly one query, so there is nothing to share through
-// LDS).  The scan is bound by HBM, so the kernel keeps as many bytes in flight
-// as its registers allow: the split's page-table entries are read once up front
-// (lane i holds page p_begin + i, broadcast with a lane read), so no key load
-// waits on a table load, and every wave keeps two pages in flight ahead of the
-// one it is scoring.
+// LDS).  The query's A fragments and head weights are staged in LDS (shared by
+// the 4 waves; 64 fewer registers per wave), every wave keeps kDecDepth page(s)
+// in flight while it scores one, and the split's page-table entries are read
+// once up front (lane i holds page p_begin + i, broadcast with a lane read), so
+// no key load waits on a table load.  A wave's scores stay in registers and are
+// stored after its last page: stores and loads share one completion counter,
+// so a store between the page loads would make every later wait also wait for
+// it (measured: 20% of the scan).
 template <int H_I, int D_I>
-__global__ __launch_bounds__(256) void indexer_decode_kernel(
+__global__ __launch_bounds__(256, 2) void indexer_decode_kernel(
     const uint8_t *__restrict__ q_fp8, const float *__restrict__ q_scale, const float *__restrict__ w, int64_t w_ld,
     const uint8_t *__restrict__ key_cache, const float *__restrict__ key_scale, int64_t n_pages,
     const int32_t *__restrict__ page_table, int64_t pt_ld, const int32_t *__restrict__ q_seq,
     const int32_t *__restrict__ q_pos, int32_t n_q, float *__restrict__ scores, int64_t ld, int pages_per_split) {
     using S = IdxShape<H_I, D_I>;
+    constexpr int NH = 32 * S::HT;                   // heads rounded up to MFMA row tiles
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[NH * S::ROW];   // padded rows: conflict-free reads
+    __shared__ __attribute__((aligned(16))) float w_lds[NH];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
     const int t = blockIdx.x;
     const int pos = q_pos[t];
@@ -242,7 +254,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     if (n_pg > max_page) n_pg = max_page;
     const int64_t p_begin = (int64_t)blockIdx.y * pages_per_split;
     const int64_t p_end = min(n_pg, p_begin + pages_per_split);   // pages_per_split <= 4 kWavePages
-    if (p_begin >= p_end) return;
+    if (p_begin >= p_end) return;                    // uniform over the workgroup
     if (n_pages <= 0) {                                  // no page can be read: every score is NaN
         for (int64_t key = p_begin * kPage + threadIdx.x; key < min(p_end * kPage, min((int64_t)pos + 1, ld));
              key += 256)
@@ -260,14 +272,59 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
             if (v >= 0 && v < n_pages) my_phys = v;
         }
     }
-    QueryFrag<H_I, D_I> q;
-    load_query<H_I, D_I>(q, q_fp8, w, w_ld, t, lane);
+    // the query's FP8 rows (heads past H_I zero) and weights, once per workgroup
+    for (int c = threadIdx.x; c < NH * S::CH; c += 256) {
+        const int head = c / S::CH, col = c % S::CH;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (head < H_I) v = reinterpret_cast<const uint4 *>(q_fp8 + ((int64_t)t * H_I + head) * D_I)[col];
+        *reinterpret_cast<uint4 *>(&q_lds[head * S::ROW + col * 16]) = v;
+    }
+    for (int hh = threadIdx.x; hh < NH; hh += 256) w_lds[hh] = hh < H_I ? w[(int64_t)t * w_ld + hh] : 0.0f;
     const float qs = q_scale[t];
+    __syncthreads();
+
+    // Score of key `lane` of a page whose B fragments are in `b` (same mapping
+    // as page_scores, with A fragments and weights read from LDS).
+    auto scores_of = [&](const i32x8 (&b)[2][S::KC]) -> float {
+        float part[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x16 acc[S::HT];
+#pragma unroll
+            for (int ht = 0; ht < S::HT; ++ht) {
+                acc[ht] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                const uint8_t *qrow = &q_lds[(32 * ht + (lane & 31)) * S::ROW + g * S::HALF];
+#pragma unroll
+                for (int c = 0; c < S::KC; ++c) {
+                    const uint4 lo = *reinterpret_cast<const uint4 *>(qrow + 32 * c);
+                    const uint4 hi = *reinterpret_cast<const uint4 *>(qrow + 32 * c + 16);
+                    const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    acc[ht] = mfma_f8_32x32x64(a, b[kt][c], acc[ht]);
+                }
+            }
+            float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+            for (int ht = 0; ht < S::HT; ++ht) {
+#pragma unroll
+                for (int i = 0; i < 16; i += 4) {
+                    // accumulator element i: head 32 ht + 8 (i / 4) + 4 g + i % 4
+                    const float4 wv = *reinterpret_cast<const float4 *>(&w_lds[32 * ht + 2 * i + 4 * g]);
+                    s0 = fmaf(wv.x, relu_bits(acc[ht][i + 0]), s0);
+                    s1 = fmaf(wv.y, relu_bits(acc[ht][i + 1]), s1);
+                    s2 = fmaf(wv.z, relu_bits(acc[ht][i + 2]), s2);
+                    s3 = fmaf(wv.w, relu_bits(acc[ht][i + 3]), s3);
+                }
+            }
+            part[kt] = (s0 + s1) + (s2 + s3);
+        }
+        // lane i < 32: key i (tile 0); lane 32 + i: key 32 + i (tile 1)
+        return halves_reduce_scatter(part[0], part[1]);
+    };
 
     // Page slot m of this wave is page p_begin + wave + 4 m.  Every wave runs all
     // kWavePages slots, fully unrolled and branch-free: a slot past the split
     // loads a page of the split again and stores nothing.  With no loop back-edge
-    // the compiler can wait for exactly the page being scored while the next two
+    // the compiler can wait for exactly the page being scored while the next ones
     // stay in flight.
     auto fetch = [&](int m, i32x8 (&b)[2][S::KC], float &ksc) {
         const int64_t p = min(p_begin + wave + 4 * m, p_end - 1);
@@ -287,21 +344,28 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
         const float k = key_scale[(int64_t)phys * kPage + lane];
         ksc = phys0 < 0 ? __builtin_nanf("") : k;
     };
+    float sreg[kWavePages];
     auto score = [&](int m, const i32x8 (&b)[2][S::KC], float ksc) {
-        const int64_t p = p_begin + wave + 4 * m;
-        const float sc = page_scores<H_I, D_I>(q, b);
-        const int64_t key = p * kPage + lane;
-        if (p < p_end && key <= pos && key < ld) scores[(int64_t)t * ld + key] = sc * (qs * ksc);
+        const float sc = scores_of(b);
+        sreg[m] = sc * (qs * ksc);
     };
 
-    i32x8 bf[3][2][S::KC];
-    float kf[3];
-    fetch(0, bf[0], kf[0]);
-    fetch(1, bf[1], kf[1]);
+    constexpr int D = kDecDepth + 1;                 // ring slots: in flight + the one scored
+    i32x8 bf[D][2][S::KC];
+    float kf[D];
+#pragma unroll
+    for (int m = 0; m < kDecDepth; ++m) fetch(m, bf[m], kf[m]);
 #pragma unroll
     for (int m = 0; m < kWavePages; ++m) {
-        if (m + 2 < kWavePages) fetch(m + 2, bf[(m + 2) % 3], kf[(m + 2) % 3]);
-        score(m, bf[m % 3], kf[m % 3]);
+        if (m + kDecDepth < kWavePages) fetch(m + kDecDepth, bf[(m + kDecDepth) % D], kf[(m + kDecDepth) % D]);
+        score(m, bf[m % D], kf[m % D]);
+    }
+    const int64_t k_end = min(p_end * kPage, min((int64_t)pos + 1, ld));
+    float *srow = scores + (int64_t)t * ld;
+#pragma unroll
+    for (int m = 0; m < kWavePages; ++m) {
+        const int64_t key = (p_begin + wave + 4 * m) * kPage + lane;
+        if (key < k_end) srow[key] = sreg[m];
     }
 }
 
