@@ -63,6 +63,11 @@ __device__ __forceinline__ void load_query(QueryFrag<H_I, D_I> &q, const uint8_t
     }
 }
 
+// max(x, 0) on the bit pattern: one integer max, where the float max of an
+// MFMA result first has to quiet a possible signalling NaN.  Equal to the
+// float max for every number.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // One query against one 64-key page whose B fragments are in `b`.
 // Returns the (unscaled) score of key `lane` of the page.
 template <int H_I, int D_I>
@@ -84,10 +89,10 @@ __device__ __forceinline__ float page_scores(const QueryFrag<H_I, D_I> &q,
         for (int ht = 0; ht < S::HT; ++ht) {
 #pragma unroll
             for (int i = 0; i < 16; i += 4) {
-                s0 = fmaf(q.w[ht][i + 0], fmaxf(acc[ht][i + 0], 0.0f), s0);
-                s1 = fmaf(q.w[ht][i + 1], fmaxf(acc[ht][i + 1], 0.0f), s1);
-                s2 = fmaf(q.w[ht][i + 2], fmaxf(acc[ht][i + 2], 0.0f), s2);
-                s3 = fmaf(q.w[ht][i + 3], fmaxf(acc[ht][i + 3], 0.0f), s3);
+                s0 = fmaf(q.w[ht][i + 0], relu_bits(acc[ht][i + 0]), s0);
+                s1 = fmaf(q.w[ht][i + 1], relu_bits(acc[ht][i + 1]), s1);
+                s2 = fmaf(q.w[ht][i + 2], relu_bits(acc[ht][i + 2]), s2);
+                s3 = fmaf(q.w[ht][i + 3], relu_bits(acc[ht][i + 3]), s3);
             }
         }
         part[kt] = (s0 + s1) + (s2 + s3);
@@ -219,11 +224,6 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 // ------------------------------------------------------------------ decode
 constexpr int kWavePages = 16;                    // page slots per wave (4 waves: 64 pages per split)
 constexpr int kDecDepth = 1;                      // pages per wave in flight while one is scored
-
-// max(x, 0) on the bit pattern: one integer max, where the float max of an
-// MFMA result first has to quiet a possible signalling NaN.  Equal to the
-// float max for every number.
-__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Workgroup = one query x a range of at most 64 key pages; the 4 waves take
 // pages round-robin and load B fragments straight from the cache (each key
