@@ -170,8 +170,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;     // lane half, lane within the half
     const int i16 = lane & 15, hd = (lane >> 4) & 1;
-    const int t = SPLIT ? (int)blockIdx.x / n_splits : (int)blockIdx.x;
-    const int split = SPLIT ? (int)blockIdx.x % n_splits : 0;
+    // decode: workgroup b takes query b % n_q, split b / n_q, so that the splits of
+    // a query are n_q apart in launch order and (with workgroups dealt round-robin
+    // to the 8 XCDs, n_q a multiple of 8) share one XCD's L2 for q and the indices
+    const int n_q_split = SPLIT ? (int)gridDim.x / n_splits : 0;
+    const int t = SPLIT ? (int)blockIdx.x % n_q_split : (int)blockIdx.x;
+    const int split = SPLIT ? (int)blockIdx.x / n_q_split : 0;
     const int per_split = SPLIT ? (k + n_splits - 1) / n_splits : k;
     const int i_begin = split * per_split;
     const int i_end = min(k, i_begin + per_split);
