@@ -106,6 +106,17 @@ __device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8 &a, const bf16x8 &b, 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// O^T += V^T P^T with the accumulator pinned to the AGPR file.  This file is
+// compiled with the VGPR form of the compiler's own MFMAs, so S^T lands in
+// VGPRs where the softmax reads it; the 256 O^T accumulators per lane stay in
+// AGPRs through this asm form instead of being moved between the files.  The
+// compiler does not see an MFMA here, so the required wait states are written
+// out by the caller: after VALU writes of the operands before the first one,
+// and before the accumulators are read or rewritten after the last one.
+__device__ __forceinline__ void mfma32_bf16_acc(f32x16 &c, const bf16x8 &a, const bf16x8 &b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
 // Workgroup barrier after this wave's LDS accesses and all but the newest N
 // vector-memory loads (in issue order) have completed.  The copies above are
 // invisible to the compiler's counter tracking, so every wait for them is written
@@ -440,7 +451,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                 if constexpr (f + kLookV<FP8> < kPV) vload(f + kLookV<FP8>, vlo[f % kLookV<FP8>], vhi[f % kLookV<FP8>]);
                 const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 const uint4 bw = make_uint4(pw[f >> 4][0], pw[f >> 4][1], pw[f >> 4][2], pw[f >> 4][3]);
-                o[f & 15] = mfma32_bf16(a, __builtin_bit_cast(bf16x8, bw), o[f & 15]);
+                if constexpr (f == 0) asm volatile("s_nop 4");   // P^T was just written by VALU code
+                mfma32_bf16_acc(o[f & 15], a, __builtin_bit_cast(bf16x8, bw));
                 __builtin_amdgcn_sched_barrier(0);
             });
             float tmax = FP8 ? rmax : rmax * c2;          // c2 > 0: the max of the log2 logits
@@ -469,6 +481,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
             if (j + 1 < n_tiles && step(j + 1, buf_b, buf_a)) break;
         }
         barrier_after_loads<0>();
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // the last O^T MFMA has written back
         again = sm.restart != 0;
         first_attempt = false;
         if (again) {
