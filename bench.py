@@ -26,6 +26,7 @@ counter runs are scaled by.
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--calib-copy]
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -164,7 +165,16 @@ def setup_decode_c4(dev):
     ld = int(inp.lens.max())
     ds = P.alloc_decode(cfg.decode_batch, ld, cfg.k, cfg.h, device=dev)
     torch.cuda.synchronize()
-    return cfg, inp, caches, newest, ds
+    return cfg, inp, caches, newest, ds, kv_slot
+
+
+def fp8_kv_caches(caches, inp, kv_slot):
+    """The same caches with the latent rows quantized to FP8 E4M3 + a per-token scale."""
+    kv8 = torch.zeros((inp.n_slots, 576), dtype=torch.uint8, device=caches.kv_cache.device)
+    sc8 = torch.zeros(inp.n_slots, dtype=torch.float32, device=caches.kv_cache.device)
+    dsa.kv_cache_store(inp.kv, kv_slot, kv8, sc8)
+    torch.cuda.synchronize()
+    return dataclasses.replace(caches, kv_cache=kv8, kv_scale=sc8)
 
 
 def run_decode_step(cfg, inp, caches, newest, ds, timer=None):
@@ -183,16 +193,31 @@ def run_decode_step(cfg, inp, caches, newest, ds, timer=None):
     if e: e.record()
     e = t("mla")
     dsa.sparse_mla_decode(inp.q, caches.kv_cache, inp.kv_slot_table, inp.q_seq, ds.idx, SM_SCALE, ds.out, ds.lse,
-                          n_splits=ds.n_splits, ws=ds.ws)
+                          kv_scale=caches.kv_scale, n_splits=ds.n_splits, ws=ds.ws)
     if e: e.record()
 
 
-def decode_bytes(inp, k, h):
+def time_decode(args, cfg, inp, caches, newest, ds):
+    """Warm-up, then `args.steps` timed decode steps: (seconds per step, stage ms)."""
+    for _ in range(args.warmup):
+        run_decode_step(cfg, inp, caches, newest, ds)
+    torch.cuda.synchronize()
+    timer = StageTimer(["store", "indexer", "topk", "mla"])
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_decode_step(cfg, inp, caches, newest, ds, timer)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / args.steps, timer.avg_ms()
+
+
+def decode_bytes(inp, k, h, kv_row_bytes=1152):
+    """Algorithmic HBM bytes per decode step; a latent row is 1152 B in bf16,
+    576 B of codes + a 4-byte scale in FP8."""
     n_keys = int(inp.lens.sum())
     return {
         "indexer_bytes": n_keys * (128 + 4) + inp.iq.numel() + 4.0 * n_keys,   # keys + scales read, scores written
         "topk_bytes": 4.0 * n_keys + 4.0 * inp.lens.numel() * k,
-        "mla_bytes": inp.lens.numel() * k * (1152 + 4 + 4) + inp.q.numel() * 2 + inp.lens.numel() * h * 512 * 2,
+        "mla_bytes": inp.lens.numel() * k * (kv_row_bytes + 4 + 4) + inp.q.numel() * 2 + inp.lens.numel() * h * 512 * 2,
     }
 
 
@@ -288,17 +313,8 @@ def main():
         del st, inp
         torch.cuda.empty_cache()
         log("[bench] generating the 128K-context decode inputs on the GPU")
-        dcfg, dinp, caches, newest, ds = setup_decode_c4(dev)
-        for _ in range(args.warmup):
-            run_decode_step(dcfg, dinp, caches, newest, ds)
-        torch.cuda.synchronize()
-        dtimer = StageTimer(["store", "indexer", "topk", "mla"])
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            run_decode_step(dcfg, dinp, caches, newest, ds, dtimer)
-        torch.cuda.synchronize()
-        dwall = (time.perf_counter() - t0) / args.steps
-        dst = dtimer.avg_ms()
+        dcfg, dinp, caches, newest, ds, kv_slot = setup_decode_c4(dev)
+        dwall, dst = time_decode(args, dcfg, dinp, caches, newest, ds)
         db = decode_bytes(dinp, dcfg.k, dcfg.h)
         dk = {
             "indexer": {"bound": "hbm", "achieved": db["indexer_bytes"] / (dst["indexer"] * 1e-3) / 1e9,
@@ -315,7 +331,19 @@ def main():
                             "us_per_step": dwall * 1e6, "tokens_per_s": dcfg.decode_batch / dwall,
                             "stages_us": {k2: v * 1e3 for k2, v in dst.items()}, "kernels": dk}
         log(f"[bench] decode {dwall * 1e6:.1f} us/step; stages us {result['decode']['stages_us']}")
-        del caches, dinp, ds
+        # the same step over an FP8 E4M3 latent cache (per-token scale)
+        caches = fp8_kv_caches(caches, dinp, kv_slot)
+        dwall8, dst8 = time_decode(args, dcfg, dinp, caches, newest, ds)
+        mla8 = decode_bytes(dinp, dcfg.k, dcfg.h, kv_row_bytes=576 + 4)["mla_bytes"] / (dst8["mla"] * 1e-3) / 1e9
+        result["decode_fp8_kv"] = {
+            "workload": "the decode step above over an FP8 E4M3 latent cache (576 B + fp32 scale per token)",
+            "us_per_step": dwall8 * 1e6, "tokens_per_s": dcfg.decode_batch / dwall8,
+            "stages_us": {k2: v * 1e3 for k2, v in dst8.items()},
+            "kernels": {"sparse_mla_decode": {"bound": "hbm", "achieved": mla8, "peak": PEAK_HBM, "unit": "GB/s",
+                                              "us": dst8["mla"] * 1e3, "frac": mla8 / PEAK_HBM}}}
+        log(f"[bench] decode, FP8 latent cache: {dwall8 * 1e6:.1f} us/step; stages us "
+            f"{result['decode_fp8_kv']['stages_us']}")
+        del caches, dinp, ds, kv_slot
         torch.cuda.empty_cache()
         inp = None
 

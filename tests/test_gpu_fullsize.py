@@ -199,7 +199,7 @@ def test_prefill_32k_bench_launch():
 # ------------------------------------------------------------------ decode (bench launch)
 def test_decode_bench_launch():
     say("[full C4] decode, 64 sequences x U[32768, 131072], as launched by the benchmark")
-    cfg, inp, caches, newest, ds = bench.setup_decode_c4(DEV)
+    cfg, inp, caches, newest, ds, kv_slot = bench.setup_decode_c4(DEV)
     bench.run_decode_step(cfg, inp, caches, newest, ds)
     torch.cuda.synchronize()
     B, k = cfg.decode_batch, cfg.k
@@ -245,6 +245,19 @@ def test_decode_bench_launch():
     el = float(np.abs(ds.lse.cpu().numpy() - ref_l).max())
     say(f"  MLA decode, all 64 queries: out max-abs-rel {e:.3e}, lse max abs err {el:.3e}")
     assert e <= TOL_BF16 and el <= 2e-2
+    # the same indices over an FP8 E4M3 latent cache, as the benchmark's FP8 leg launches it
+    caches8 = bench.fp8_kv_caches(caches, inp, kv_slot)
+    out8, lse8 = torch.empty_like(ds.out), torch.empty_like(ds.lse)
+    dsa.sparse_mla_decode(inp.q, caches8.kv_cache, inp.kv_slot_table, inp.q_seq, ds.idx, SM_SCALE, out8, lse8,
+                          kv_scale=caches8.kv_scale, n_splits=ds.n_splits, ws=ds.ws)
+    torch.cuda.synchronize()
+    codes, scales = oracle.kv_quantize(packed_full)
+    ref_o8, ref_l8 = oracle.sparse_mla(bits16(inp.q), codes, new_idx, SM_SCALE, kv_scale=scales,
+                                       n_threads=oracle_threads())
+    e8 = max_abs_rel(out8.float().cpu().numpy(), ref_o8)
+    el8 = float(np.abs(lse8.cpu().numpy() - ref_l8).max())
+    say(f"  MLA decode, FP8 latent cache: out max-abs-rel {e8:.3e}, lse max abs err {el8:.3e}")
+    assert e8 <= TOL_FP8 and el8 <= 2e-2
 
 
 # ------------------------------------------------------------------ chunked prefill, FP8 KV

@@ -331,13 +331,15 @@ def test_chunked_equals_monolithic():
 
 
 # ------------------------------------------------------------------ decode
-@pytest.mark.parametrize("batch,lo,hi,n_splits", [(8, 2000, 9000, 0), (5, 100, 3000, 3), (3, 2049, 2049, 1)])
-def test_decode_vs_oracle(batch, lo, hi, n_splits):
-    say(f"[decode] B={batch} ctx=[{lo},{hi}] splits={n_splits}")
+@pytest.mark.parametrize("batch,lo,hi,n_splits,kv_fp8", [(8, 2000, 9000, 0, False), (5, 100, 3000, 3, False),
+                                                         (3, 2049, 2049, 1, False), (6, 1500, 7000, 0, True),
+                                                         (4, 2049, 4100, 2, True)])
+def test_decode_vs_oracle(batch, lo, hi, n_splits, kv_fp8):
+    say(f"[decode] B={batch} ctx=[{lo},{hi}] splits={n_splits} fp8={kv_fp8}")
     c = CONFIGS["C4"]
     inp = synth.make_decode(c, batch=batch, ctx_lo=lo, ctx_hi=hi)
     d = lambda x: x.to(DEV)
-    caches = P.alloc_prefill(inp.n_pages, c.d_i, inp.n_slots, 1, 1, c.k, c.h)
+    caches = P.alloc_prefill(inp.n_pages, c.d_i, inp.n_slots, 1, 1, c.k, c.h, kv_fp8=kv_fp8)
     kv_slot = torch.empty(inp.n_slots, dtype=torch.int64)
     for b in range(batch):
         s0, nb = int(inp.seq_start[b]), int(inp.lens[b])
@@ -361,18 +363,26 @@ def test_decode_vs_oracle(batch, lo, hi, n_splits):
         assert (np.abs(g[b, :nb] - ref[b, :nb]) <= BOUND_C * A[0] + 1e-30).all(), b
     np.testing.assert_array_equal(ds.idx.cpu().numpy(), oracle.topk(g, pos, c.k))
     idx = ds.idx.cpu().numpy()
-    ref_o, ref_l = oracle.sparse_mla(bits16(inp.q), bits16(inp.kv), idx, SM_SCALE,
-                                     seq_start=inp.seq_start.numpy(), q_seq=inp.q_seq.numpy(),
-                                     n_threads=oracle_threads())
+    if kv_fp8:
+        codes, scales = oracle.kv_quantize(bits16(inp.kv))
+        ref_o, ref_l = oracle.sparse_mla(bits16(inp.q), codes, idx, SM_SCALE, kv_scale=scales,
+                                         seq_start=inp.seq_start.numpy(), q_seq=inp.q_seq.numpy(),
+                                         n_threads=oracle_threads())
+    else:
+        ref_o, ref_l = oracle.sparse_mla(bits16(inp.q), bits16(inp.kv), idx, SM_SCALE,
+                                         seq_start=inp.seq_start.numpy(), q_seq=inp.q_seq.numpy(),
+                                         n_threads=oracle_threads())
+    tol = TOL_FP8 if kv_fp8 else TOL_BF16
     e = max_abs_rel(ds.out.float().cpu().numpy(), ref_o)
     say(f"  decode out max-abs-rel = {e:.3e}")
-    assert e <= TOL_BF16
+    assert e <= tol
     assert float(np.abs(ds.lse.cpu().numpy() - ref_l).max()) <= 2e-2
     # the prefill-form kernel on the same indices agrees within tolerance
     out2 = torch.empty_like(ds.out)
-    dsa.sparse_mla_prefill(d(inp.q), caches.kv_cache, d(inp.kv_slot_table), d(inp.q_seq), ds.idx, SM_SCALE, out2)
+    dsa.sparse_mla_prefill(d(inp.q), caches.kv_cache, d(inp.kv_slot_table), d(inp.q_seq), ds.idx, SM_SCALE, out2,
+                           kv_scale=caches.kv_scale)
     torch.cuda.synchronize()
-    assert max_abs_rel(out2.float().cpu().numpy(), ref_o) <= TOL_BF16
+    assert max_abs_rel(out2.float().cpu().numpy(), ref_o) <= tol
 
 
 def test_decode_row_matches_prefill_row():
