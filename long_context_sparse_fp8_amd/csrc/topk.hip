@@ -6,8 +6,10 @@
 // row with no more than k candidates keeps all of them (the dense
 // degeneration of the deployment article, section 5.1).
 //
-// One workgroup of 1024 threads per row; the work is bound by vector ALU
-// operations per score, so every score is touched by only three cheap sweeps:
+// One workgroup per row: 512 threads when many rows of at most 32K scores are
+// selected at once (two workgroups share a CU, so one row's barriers and loads
+// overlap the other's work), else 1024.  Every score is touched by only three
+// cheap sweeps:
 //   1. an 11-bit histogram of the top key bits (sign, exponent, two mantissa
 //      bits) in LDS, eight lane-interleaved copies; a block scan of the 2048
 //      bins from the top finds the bin holding the k-th largest key;
@@ -22,12 +24,12 @@
 //      its bit in an LDS bitmap of the row; a block scan of the bitmap words'
 //      popcounts then writes the kept indices in ascending order.
 // Scores become order-preserving uint32 keys.  The row is cut into chunks of
-// 4096 scores; in chunk c thread i owns the four consecutive scores starting at
-// c * 4096 + 4 i, so every wave-wide load is one contiguous 1 KB run.  Rows of
-// at most 4096 * C scores are read once and kept in registers (every prefill
-// row here); longer rows are streamed chunk by chunk for each sweep (they are
-// few: one per decode sequence, and the re-reads hit L2).  Everything is
-// integer, so the selection is exact for the given scores.
+// 4 NT scores (NT threads); in chunk c thread i owns the four consecutive
+// scores starting at c * 4 NT + 4 i, so every wave-wide load is one contiguous
+// 1 KB run.  Rows of at most 4 NT C scores are read once and kept in registers
+// (every prefill row here); longer rows are streamed chunk by chunk for each
+// sweep (they are few: one per decode sequence, and the re-reads hit L2).
+// Everything is integer, so the selection is exact for the given scores.
 //
 // Few long rows (decode: one row of up to 128K scores per sequence) would leave
 // most of the chip idle with one workgroup per row.  With a workspace, such a
@@ -45,34 +47,45 @@
 
 namespace dsa {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kChunk = 4 * kTopkThreads;        // scores per chunk
 constexpr int kBins0 = 2048;                    // first digit: key bits 31..21
-constexpr int kCopies0 = 8;                     // lane-interleaved copies of the first histogram
-constexpr int kCandCap = 8192;                  // candidate list capacity
 constexpr int kBins = 512;                      // later digits (<= 9 bits)
-constexpr int kCopies = 4;
-constexpr int kWords = (int)(kTopkMaxRow / 32); // bitmap words
+constexpr int kCopies = 4;                      // lane-interleaved copies of the later histograms
 
+// Workgroup shape: NT threads (1024, or 512 for rows of at most 32K scores,
+// two workgroups per CU), chunks of 4 NT scores; C > 0 chunks per row in
+// registers, C == 0 streamed.
+template <int NT, int C>
+struct TopkShape {
+    static constexpr int kWaves = NT / kWave;
+    static constexpr int kChunk = 4 * NT;                            // scores per chunk
+    static constexpr int kCopies0 = NT / 128;                        // copies of the first histogram
+    static constexpr int kCandCap = 8 * NT;                          // candidate list capacity
+    static constexpr int64_t kMaxRow = C > 0 ? (int64_t)C * 4 * NT : kTopkMaxRow;
+    static constexpr int kWords = (int)(kMaxRow / 32);               // bitmap words
+    static constexpr int kBinsPer = kBins0 / NT;                     // first-digit bins per thread in the scan
+};
+
+template <int NT, int C>
 struct TopkSmem {
+    using S = TopkShape<NT, C>;
     union {
-        uint32_t hist0[kBins0 * kCopies0];      // hist0[bin * 8 + lane % 8]
+        uint32_t hist0[kBins0 * S::kCopies0];   // hist0[bin * kCopies0 + lane % kCopies0]
         struct {
-            uint32_t key[kCandCap];
-            int32_t idx[kCandCap];
+            uint32_t key[S::kCandCap];
+            int32_t idx[S::kCandCap];
         } cand;
     };
     uint32_t hist[kBins * kCopies];             // hist[bin * 4 + lane % 4]
-    uint32_t bitmap[kWords];
+    uint32_t bitmap[S::kWords];
     int32_t stage[kTopkMaxK];
-    uint32_t wsum[kTopkWaves];
+    uint32_t wsum[S::kWaves];
     uint32_t sel_bin, sel_rem, sel_done, n_cand;
 };
 
-// Block-wide exclusive scan (all 1024 threads call it); returns the sum over
+// Block-wide exclusive scan (all NT threads call it); returns the sum over
 // lower threads, `total` gets the block sum.
-__device__ __forceinline__ uint32_t block_excl_scan(TopkSmem &sm, uint32_t a, uint32_t &total) {
+template <int NT, int C>
+__device__ __forceinline__ uint32_t block_excl_scan(TopkSmem<NT, C> &sm, uint32_t a, uint32_t &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t ia = a;
 #pragma unroll
@@ -84,7 +97,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(TopkSmem &sm, uint32_t a, ui
     __syncthreads();
     uint32_t pre = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
+    for (int w = 0; w < NT / kWave; ++w) {
         const uint32_t x = sm.wsum[w];
         pre += w < wave ? x : 0u;
         tot += x;
@@ -94,12 +107,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(TopkSmem &sm, uint32_t a, ui
     return pre + ia - a;
 }
 
-// Keys of one chunk for the calling thread: scores c*4096 + 4*tid + e, e = 0..3.
+// Keys of one chunk for the calling thread: scores 4 NT c + 4 tid + e, e = 0..3.
 // Branch-free: the load address is clamped into the row and keys past n are
 // zeroed afterwards, so every load of a row is issued before the first wait.
-template <bool VEC>
+template <int NT, bool VEC>
 __device__ __forceinline__ void load_chunk(const float *row, int n, int c, uint32_t (&key)[4]) {
-    const int i = c * kChunk + 4 * (int)threadIdx.x;
+    const int i = c * 4 * NT + 4 * (int)threadIdx.x;
     float x[4];
     if constexpr (VEC) {   // row 16-byte aligned; ceil4(n) <= ld
         const float4 v = *reinterpret_cast<const float4 *>(row + min(i, ((n + 3) & ~3) - 4));
@@ -120,7 +133,8 @@ __device__ __forceinline__ void load_chunk(const float *row, int n, int c, uint3
 // holds the rem-th element.  Wave 0 only; the caller synchronises.  Kept out of
 // line: inlined, its reads get scheduled into the callers' loops and pin
 // registers for the whole kernel.
-__device__ __noinline__ void pick_digit(TopkSmem &sm, int nb, uint32_t rem, bool desc) {
+template <int NT, int C>
+__device__ __noinline__ void pick_digit(TopkSmem<NT, C> &sm, int nb, uint32_t rem, bool desc) {
     const int lane = threadIdx.x & 63;
     uint32_t c[8];   // lane owns 8 consecutive bins in scan order (nb <= 512)
     uint32_t tot = 0;
@@ -171,13 +185,15 @@ __device__ __forceinline__ int topk_row_parts(int n, int k, int parts) {
 // otherwise the part's k survivors (original index and score) go to the
 // workspace at [t, part].  kMerge: the survivors of row t (rows of one part are
 // done already).
-template <int C, bool VEC, int MODE>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
+template <int NT, int C, bool VEC, int MODE>
+__global__ __launch_bounds__(NT, 1024 / NT) void topk_kernel(const float *__restrict__ scores, int64_t ld,
                                                              const int32_t *__restrict__ q_pos, int32_t k,
                                                              int32_t *__restrict__ idx, int32_t parts,
                                                              float *__restrict__ ws_score,
                                                              int32_t *__restrict__ ws_idx) {
-    __shared__ __attribute__((aligned(16))) TopkSmem sm;
+    using S = TopkShape<NT, C>;
+    constexpr int kChunk = S::kChunk, kCopies0 = S::kCopies0;
+    __shared__ __attribute__((aligned(16))) TopkSmem<NT, C> sm;
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int64_t n64 = (int64_t)q_pos[t] + 1;
@@ -207,7 +223,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
     }
 
     if (n <= k) {   // every candidate is kept (a whole row, or a row of one part)
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+        for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
         return;
     }
     const int nc = (n + kChunk - 1) / kChunk;   // chunks of this row (uniform)
@@ -217,7 +233,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             if (c < nc) {
-                load_chunk<VEC>(row, n, c, reg[c]);
+                load_chunk<NT, VEC>(row, n, c, reg[c]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) reg[c][e] = 0u;
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
         } else {
             for (int c = 0; c < nc; ++c) {
                 uint32_t key[4];
-                load_chunk<VEC>(row, n, c, key);
+                load_chunk<NT, VEC>(row, n, c, key);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = c * kChunk + 4 * tid + e;
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
     using Checked = std::integral_constant<bool, true>;
     using Unchecked = std::integral_constant<bool, false>;
     auto clear = [&](uint32_t *p, int words) {
-        for (int i = tid; i < words / 4; i += kTopkThreads) reinterpret_cast<uint4 *>(p)[i] = make_uint4(0, 0, 0, 0);
+        for (int i = tid; i < words / 4; i += NT) reinterpret_cast<uint4 *>(p)[i] = make_uint4(0, 0, 0, 0);
     };
 
     // ---- sweep 1: 11-bit histogram of the top key bits
@@ -271,26 +287,35 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
     uint32_t rem;
     uint32_t b0;
     {
-        // thread tid owns bins 2047 - 2 tid and 2046 - 2 tid (scan order: descending)
-        uint32_t ca = 0, cb = 0;
-        const uint4 *pa = reinterpret_cast<const uint4 *>(sm.hist0 + (kBins0 - 1 - 2 * tid) * kCopies0);
-        const uint4 *pb = reinterpret_cast<const uint4 *>(sm.hist0 + (kBins0 - 2 - 2 * tid) * kCopies0);
-        const uint4 a0 = pa[0], a1 = pa[1], c0 = pb[0], c1 = pb[1];
-        ca = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w));
-        cb = ((c0.x + c0.y) + (c0.z + c0.w)) + ((c1.x + c1.y) + (c1.z + c1.w));
-        if (C > 0 && tid == kTopkThreads - 1) cb -= (uint32_t)(nc * kChunk - n);   // padding keys in bin 0
+        // thread tid owns bins 2047 - B tid - j, j = 0 .. B-1 (scan order: descending), B = 2048 / NT
+        constexpr int B = S::kBinsPer;
+        uint32_t cnt[B], mine = 0;
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const uint32_t *hb = sm.hist0 + (kBins0 - 1 - B * tid - j) * kCopies0;
+            uint32_t c = 0;
+#pragma unroll
+            for (int q = 0; q < kCopies0; q += 4) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(hb + q);
+                c += (v.x + v.y) + (v.z + v.w);
+            }
+            cnt[j] = c;
+        }
+        if (C > 0 && tid == NT - 1) cnt[B - 1] -= (uint32_t)(nc * kChunk - n);   // padding keys in bin 0
+#pragma unroll
+        for (int j = 0; j < B; ++j) mine += cnt[j];
         uint32_t total;
-        const uint32_t excl = block_excl_scan(sm, ca + cb, total);
+        uint32_t excl = block_excl_scan(sm, mine, total);
         const uint32_t kk = (uint32_t)k;
-        if (excl < kk && excl + ca + cb >= kk) {
-            if (excl + ca >= kk) {
-                sm.sel_bin = (uint32_t)(kBins0 - 1 - 2 * tid);
-                sm.sel_rem = kk - excl;
-                sm.sel_done = (excl + ca == kk) ? 1u : 0u;
-            } else {
-                sm.sel_bin = (uint32_t)(kBins0 - 2 - 2 * tid);
-                sm.sel_rem = kk - excl - ca;
-                sm.sel_done = (excl + ca + cb == kk) ? 1u : 0u;
+        if (excl < kk && excl + mine >= kk) {
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                if (excl < kk && excl + cnt[j] >= kk) {
+                    sm.sel_bin = (uint32_t)(kBins0 - 1 - B * tid - j);
+                    sm.sel_rem = kk - excl;
+                    sm.sel_done = (excl + cnt[j] == kk) ? 1u : 0u;
+                }
+                excl += cnt[j];
             }
         }
         __syncthreads();
@@ -314,7 +339,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
         uint32_t total;
         uint32_t pos = block_excl_scan(sm, mine, total);   // also orders hist0 reads before the list writes
         n_cand = total;
-        use_list = total <= (uint32_t)kCandCap;
+        use_list = total <= (uint32_t)S::kCandCap;
         if (use_list) {
             each_row([&](uint32_t key, int i) {
                 if ((key >> 21) == b0) {
@@ -331,11 +356,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
     // from memory so that the register copy stays out of the pass loops
     auto each_live = [&](auto fn) {
         if (use_list) {
-            for (int j = tid; j < (int)n_cand; j += kTopkThreads) fn(sm.cand.key[j], sm.cand.idx[j]);
+            for (int j = tid; j < (int)n_cand; j += NT) fn(sm.cand.key[j], sm.cand.idx[j]);
         } else {
             for (int c = 0; c < nc; ++c) {
                 uint32_t key[4];
-                load_chunk<VEC>(row, n, c, key);
+                load_chunk<NT, VEC>(row, n, c, key);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = c * kChunk + 4 * tid + e;
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
     });
     __syncthreads();
     {
-        const int W = (nwords + kTopkThreads - 1) / kTopkThreads;   // words per thread, in order
+        const int W = (nwords + NT - 1) / NT;   // words per thread, in order
         const int w0 = min(nwords, tid * W), w1 = min(nwords, w0 + W);
         uint32_t cnt = 0;
         for (int w = w0; w < w1; ++w) cnt += (uint32_t)__builtin_popcount(sm.bitmap[w]);
@@ -423,17 +448,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
     }
     __syncthreads();
     if (MODE == kWholeRow || (MODE == kPart && n_parts == 1)) {
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = sm.stage[i];
+        for (int i = tid; i < k; i += NT) out[i] = sm.stage[i];
     } else if (MODE == kPart) {
         const int64_t o = ((int64_t)t * parts + blockIdx.y) * k;
-        for (int i = tid; i < k; i += kTopkThreads) {
+        for (int i = tid; i < k; i += NT) {
             const int pos = sm.stage[i];
             ws_idx[o + i] = base + pos;
             ws_score[o + i] = row[pos];
         }
     } else {
         const int32_t *map = ws_idx + (int64_t)t * parts * k;
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = map[sm.stage[i]];
+        for (int i = tid; i < k; i += NT) out[i] = map[sm.stage[i]];
     }
 }
 
@@ -456,17 +481,29 @@ size_t topk_ws_bytes(int32_t n_q, int64_t ld, int32_t k) {
 template <int MODE>
 static void launch_rows(dim3 grid, int64_t len, bool vec, const float *scores, int64_t ld, const int32_t *q_pos,
                         int32_t k, int32_t *idx, int parts, float *ws_score, int32_t *ws_idx, hipStream_t stream) {
-    const dim3 block(kTopkThreads);
-#define DSA_TOPK_GO(C, V)                                                                                        \
-    hipLaunchKernelGGL((topk_kernel<C, V, MODE>), grid, block, 0, stream, scores, ld, q_pos, k, idx, parts, ws_score, \
-                       ws_idx)
+#define DSA_TOPK_GO(NT, C, V)                                                                                    \
+    hipLaunchKernelGGL((topk_kernel<NT, C, V, MODE>), grid, dim3(NT), 0, stream, scores, ld, q_pos, k, idx, parts,    \
+                       ws_score, ws_idx)
+    if constexpr (MODE == kWholeRow) {
+        // many rows: two workgroups of 512 per CU while a row fits their registers
+        if (len <= 16 * 2048) {
+            if (vec) {
+                if (len <= 8 * 2048) DSA_TOPK_GO(512, 8, true);
+                else DSA_TOPK_GO(512, 16, true);
+            } else {
+                if (len <= 8 * 2048) DSA_TOPK_GO(512, 8, false);
+                else DSA_TOPK_GO(512, 16, false);
+            }
+            return;
+        }
+    }
     if (vec) {
-        if (len <= 4 * kChunk) DSA_TOPK_GO(4, true);
-        else if (len <= 8 * kChunk) DSA_TOPK_GO(8, true);
-        else DSA_TOPK_GO(0, true);
+        if (len <= 4 * 4096) DSA_TOPK_GO(1024, 4, true);
+        else if (len <= 8 * 4096) DSA_TOPK_GO(1024, 8, true);
+        else DSA_TOPK_GO(1024, 0, true);
     } else {
-        if (len <= 8 * kChunk) DSA_TOPK_GO(8, false);
-        else DSA_TOPK_GO(0, false);
+        if (len <= 8 * 4096) DSA_TOPK_GO(1024, 8, false);
+        else DSA_TOPK_GO(1024, 0, false);
     }
 #undef DSA_TOPK_GO
 }
