@@ -92,7 +92,13 @@ const char *dsa_last_error(void);
  *   k_scale         [n] fp32 per-token scale
  *   slot            [n] int64, slot of token i = physical_page * 64 + offset;
  *                   a slot outside [0, n_pages * 64) is skipped
- *   key_cache       [n_pages, 64, d_i] E4M3 codes (written)
+ *   key_cache       n_pages pages of 64 * d_i E4M3 codes (written), each page
+ *                   fragment-major: a run of 1 KB blocks where block
+ *                   (kt * d_i / 64 + c) * 2 + h, 16-byte slot l (l < 64) holds
+ *                   bytes g * d_i / 2 + 32 c + 16 h .. +16 of the page's key
+ *                   32 kt + l % 32, g = l / 32 (kt < 2, c < d_i / 64, h < 2).
+ *                   The scorers load each block as one contiguous 1 KB run that
+ *                   is already their FP8 MFMA operand.
  *   key_scale_cache [n_pages, 64] fp32 (written)
  * A byte copy.  d_i in {64, 128}; n >= 0 (n == 0 enqueues nothing). */
 dsa_status dsa_indexer_cache_store(const uint8_t *k_fp8, const float *k_scale, const int64_t *slot,

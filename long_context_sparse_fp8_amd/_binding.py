@@ -97,8 +97,8 @@ def abi_version():
 
 # ---------------------------------------------------------------- cache stores
 def indexer_cache_store(k_fp8, k_scale, slot, key_cache, key_scale_cache, stream=None):
-    """k_fp8 [n, d_i] uint8; k_scale [n] f32; slot [n] int64 -> key_cache [n_pages, 64, d_i] uint8,
-    key_scale_cache [n_pages, 64] f32 (in place)."""
+    """k_fp8 [n, d_i] uint8; k_scale [n] f32; slot [n] int64 -> key_cache [n_pages, 64, d_i] uint8
+    (each page in the fragment-major byte order of dsa.h), key_scale_cache [n_pages, 64] f32 (in place)."""
     n, d_i = k_fp8.shape
     n_pages = key_cache.shape[0]
     assert key_cache.shape[1:] == (PAGE, d_i) and key_scale_cache.shape == (n_pages, PAGE)

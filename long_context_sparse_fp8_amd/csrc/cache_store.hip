@@ -25,7 +25,9 @@ __global__ void indexer_store_kernel(const uint8_t *__restrict__ k, const float 
     int64_t sl = slot[tok];
     if (sl < 0 || sl >= n_slots) return;
     const uint4 v = reinterpret_cast<const uint4 *>(k + tok * d_i)[c];
-    reinterpret_cast<uint4 *>(cache + sl * d_i)[c] = v;
+    const int64_t page = sl / kPage;
+    const int key = (int)(sl - page * kPage);
+    *reinterpret_cast<uint4 *>(cache + page * (kPage * d_i) + idx_key_piece_offset(key, c, d_i)) = v;
     if (c == 0) scache[sl] = ks[tok];
 }
 

@@ -10,6 +10,19 @@ namespace dsa {
 // shape); larger calls use the query-blocked one (prefill shape).
 constexpr int kIndexerDecodeMaxQ = 256;
 
+// Indexer key pages (64 keys of d_i E4M3 bytes) are stored fragment-major: the
+// page is a run of 1 KB blocks, block ((kt * d_i / 64) + c) * 2 + h holding in
+// slot l (16 bytes) the bytes 32 c + 16 h .. +16 of the lane-group half
+// g = l / 32 (bytes [g d_i / 2, (g + 1) d_i / 2)) of key 32 kt + l % 32.  That
+// is exactly the B operand of the FP8 MFMA of the scorers (lane l: key l % 32,
+// K bytes of group g), so a wave reads each block as one contiguous 1 KB load.
+// Byte offset within the page of bytes 16 piece .. +16 of key `key`:
+__host__ __device__ constexpr int idx_key_piece_offset(int key, int piece, int d_i) {
+    const int half = d_i / 2, o = 16 * piece;
+    const int g = o / half, c = (o % half) / 32, h = (o % 32) / 16;
+    return (((key / 32) * (d_i / 64) + c) * 2 + h) * 1024 + (32 * g + key % 32) * 16;
+}
+
 // Top-k limits: k <= kTopkMaxK, score rows of at most kTopkMaxRow columns.
 constexpr int kTopkMaxK = 2048;
 constexpr int64_t kTopkMaxRow = 262144;

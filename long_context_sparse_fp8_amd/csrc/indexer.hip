@@ -114,10 +114,10 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     constexpr int QB = 4 * QPW;
     constexpr int kChunks = kPage * S::CH;             // 16-byte chunks per page
     constexpr int kPer = (kChunks + 255) / 256;        // per thread
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kPage * S::ROW];
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kPage * D_I];   // pages as stored (fragment-major)
     __shared__ float sbuf[2][kPage];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nqb = (n_q + QB - 1) / QB;
     const int t0 = (nqb - 1 - (int)blockIdx.x) * QB;   // latest (longest) query blocks first
 
@@ -176,10 +176,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
                 const int ch = threadIdx.x + 256 * j;
-                if (ch < kChunks) {
-                    const int key = ch / S::CH, col = ch % S::CH;
-                    *reinterpret_cast<uint4 *>(&kbuf[buf][key * S::ROW + col * 16]) = stage[j];
-                }
+                if (ch < kChunks) *reinterpret_cast<uint4 *>(&kbuf[buf][16 * ch]) = stage[j];
             }
             if (threadIdx.x < kPage) sbuf[buf][threadIdx.x] = sstage;
         };
@@ -195,11 +192,11 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
             i32x8 b[2][S::KC];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                const uint8_t *row = &kbuf[buf][(32 * kt + (lane & 31)) * S::ROW + g * S::HALF];
 #pragma unroll
                 for (int c = 0; c < S::KC; ++c) {
-                    const uint4 lo = *reinterpret_cast<const uint4 *>(row + 32 * c);
-                    const uint4 hi = *reinterpret_cast<const uint4 *>(row + 32 * c + 16);
+                    const uint8_t *blk = &kbuf[buf][(kt * S::KC + c) * 2048 + 16 * lane];
+                    const uint4 lo = *reinterpret_cast<const uint4 *>(blk);
+                    const uint4 hi = *reinterpret_cast<const uint4 *>(blk + 1024);
                     b[kt][c] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 }
@@ -335,9 +332,8 @@ __global__ __launch_bounds__(256, 2) void indexer_decode_kernel(
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int c = 0; c < S::KC; ++c) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(base + (32 * kt + (lane & 31)) * D_I +
-                                                                   g * S::HALF + 32 * c);
-                const uint4 lo = src[0], hi = src[1];
+                const uint4 *src = reinterpret_cast<const uint4 *>(base + (kt * S::KC + c) * 2048 + 16 * lane);
+                const uint4 lo = src[0], hi = src[64];   // blocks h = 0, 1: one contiguous 1 KB load each
                 b[kt][c] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             }
         }

@@ -28,6 +28,25 @@ def u8(t):
     return t.detach().contiguous().cpu().numpy().view(np.uint8)
 
 
+def key_cache_rows(key_cache, d_i):
+    """[n_pages, 64, d_i] uint8 key cache in the stored fragment-major page order
+    -> [n_pages * 64, d_i] rows (key s of page p at row 64 p + s).  Each page is
+    a run of 1 KB blocks; block (kt * d_i / 64 + c) * 2 + h, 16-byte slot l holds
+    bytes 32 c + 16 h .. +16 of the half g = l // 32 of key 32 kt + l % 32."""
+    pages = u8(key_cache).reshape(-1, 64 * d_i)
+    half = d_i // 2
+    out = np.empty((pages.shape[0], 64, d_i), np.uint8)
+    for kt in range(2):
+        for c in range(d_i // 64):
+            for h in range(2):
+                blk = (kt * (d_i // 64) + c) * 2 + h
+                for l in range(64):
+                    g, key = l // 32, 32 * kt + l % 32
+                    b0 = g * half + 32 * c + 16 * h
+                    out[:, key, b0:b0 + 16] = pages[:, blk * 1024 + 16 * l:blk * 1024 + 16 * l + 16]
+    return out.reshape(-1, d_i)
+
+
 def max_abs_rel(gpu, ref):
     ref = np.asarray(ref, np.float64)
     gpu = np.asarray(gpu, np.float64)

@@ -24,7 +24,7 @@ import bench
 import oracle
 import synth
 from synth.configs import CONFIGS, SM_SCALE, Config
-from gpu_common import DEV, say, bits16, u8, max_abs_rel, oracle_threads
+from gpu_common import DEV, say, bits16, u8, max_abs_rel, oracle_threads, key_cache_rows
 import long_context_sparse_fp8_amd as dsa
 from long_context_sparse_fp8_amd import pipeline as P
 
@@ -187,8 +187,8 @@ def test_prefill_32k_bench_launch():
     ratio, mism = _check_index_rows(g, ref.astype(np.float64), A, pos, k, gi)
     say(f"  {len(rows)} rows: indexer err/bound max {ratio:.4f}; index mismatches (near-ties) {mism}")
     # cache contents are the stored tokens, at their shuffled places
-    kc = st.key_cache.view(-1, cfg.d_i)[_sel(inp.ik_slot, rows).to(DEV)].cpu()
-    assert torch.equal(kc, _sel(inp.ik, rows))
+    kc = key_cache_rows(st.key_cache, cfg.d_i)[_sel(inp.ik_slot, rows).numpy()]
+    assert np.array_equal(kc, u8(_sel(inp.ik, rows)))
     ref_o, ref_l = _mla_rows_ref(bits16(_sel(inp.q, rows)), bits16(inp.kv), gi)
     e = max_abs_rel(_sel(st.out, rows).float().numpy(), ref_o)
     el = float(np.abs(_sel(st.lse, rows).numpy() - ref_l).max())

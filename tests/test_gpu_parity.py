@@ -22,7 +22,7 @@ import oracle
 import synth
 from synth.configs import CONFIGS, SM_SCALE, Config
 from gpu_common import (DEV, say, bits16, u8, max_abs_rel, indexer_abs_scale, setup_prefill, run_prefill,
-                        oracle_threads)
+                        oracle_threads, key_cache_rows)
 import long_context_sparse_fp8_amd as dsa
 from long_context_sparse_fp8_amd import pipeline as P
 
@@ -53,7 +53,7 @@ def test_cache_store_bytes(cfg):
     st = setup_prefill(inp, c.k)
     torch.cuda.synchronize()
     slots = inp.ik_slot.numpy()
-    kc = u8(st.key_cache).reshape(-1, c.d_i)
+    kc = key_cache_rows(st.key_cache, c.d_i)
     np.testing.assert_array_equal(kc[slots], u8(inp.ik))
     np.testing.assert_array_equal(st.key_scale.cpu().numpy().reshape(-1)[slots], inp.ik_scale.numpy())
     kvs = inp.kv_slot_table[0].numpy()
