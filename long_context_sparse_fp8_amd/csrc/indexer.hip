@@ -203,16 +203,21 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
             }
             const float ksc = sbuf[buf][lane];
             const int64_t key = p * kPage + lane;
+            float sc[QPW];
 #pragma unroll
             for (int qq = 0; qq < QPW; ++qq) {
                 const int r = wave * QPW + qq;
-                if ((active >> r) & 1u) {
-                    const float sc = page_scores<H_I, D_I>(q[qq], b);
-                    if (key <= qp[qq] && key < ld)
-                        scores[(int64_t)(t0 + r) * ld + key] = sc * (qs[qq] * ksc);
-                }
+                sc[qq] = (active >> r) & 1u ? page_scores<H_I, D_I>(q[qq], b) : 0.0f;
             }
+            // the next page goes to LDS before the score stores: loads and stores
+            // share one counter, so a store issued first would be waited for too
             if (p + 1 < n_pg) commit(buf ^ 1);
+#pragma unroll
+            for (int qq = 0; qq < QPW; ++qq) {
+                const int r = wave * QPW + qq;
+                if (((active >> r) & 1u) && key <= qp[qq] && key < ld)
+                    scores[(int64_t)(t0 + r) * ld + key] = sc[qq] * (qs[qq] * ksc);
+            }
             __syncthreads();
         }
     }
