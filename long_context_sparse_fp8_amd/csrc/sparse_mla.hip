@@ -69,7 +69,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // for every outstanding LDS read (lgkmcnt(0)) after each copy, which drains the
 // register-ring prefetch of the MFMA operands.  The copy is tracked by vmcnt
 // only; its destination is read after an explicit s_waitcnt and a barrier.  It
-// has no register results.
+// has no register results.  m0 is a reserved register on this target, so the
+// compiler ignores the clobber (with a warning); nothing else in these kernels
+// uses m0 (the generated code sets it only in these copies).
 template <int IMM>
 __device__ __forceinline__ void g2lds16(const void *gsrc, uint32_t lds_base) {
     static_assert(IMM >= 0 && IMM < 4096, "immediate offset");
