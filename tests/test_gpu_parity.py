@@ -144,7 +144,7 @@ def test_indexer_shared_weights_and_columns_untouched():
 
 
 # ------------------------------------------------------------------ top-k
-@pytest.mark.parametrize("case", ["normal", "ties", "zeros", "short_rows", "wide", "odd_ld", "mid",
+@pytest.mark.parametrize("case", ["normal", "ties", "zeros", "short_rows", "wide", "odd_ld", "mid", "mid_ties",
                                   "split_ties", "split_mixed"])
 def test_topk_bitexact_from_identical_scores(case):
     say(f"[topk] {case}")
@@ -156,11 +156,15 @@ def test_topk_bitexact_from_identical_scores(case):
         n_q, ld, k = 50, 20001, 2048
     if case == "mid":               # register-resident rows of the 16K..32K variant
         n_q, ld, k = 64, 32768, 1000
+    if case == "mid_ties":          # 32K rows whose threshold bin overflows the candidate list
+        n_q, ld, k = 300, 32768, 2048
     if case in ("split_ties", "split_mixed"):   # few long rows: split over workgroups
         n_q, ld, k = 64, 40000, 333 if case == "split_ties" else 2048
     s = rng.standard_normal((n_q, ld)).astype(np.float32)
     if case in ("ties", "split_ties"):
         s = np.round(s * 2) / 2
+    if case == "mid_ties":          # 23% of a row ties at the top value: more than the list holds
+        s = np.round(np.minimum(s, 1.0) * 2) / 2
     if case == "zeros":
         s[:, ::2] = 0.0
         s[:, 1::4] = -0.0
