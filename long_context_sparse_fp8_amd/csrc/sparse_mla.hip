@@ -293,10 +293,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                 uint32_t o8[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wds[e], false);   // bytes 0, 1
-                    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wds[e], true);    // bytes 2, 3
-                    bf16x2 b0 = {(__bf16)lo[0], (__bf16)lo[1]};
-                    bf16x2 b1 = {(__bf16)hi[0], (__bf16)hi[1]};
+                    // E4M3 -> bf16 is exact (scale 1): one instruction per two codes
+                    const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[e], 1.0f, false);  // bytes 0, 1
+                    const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[e], 1.0f, true);   // bytes 2, 3
                     o8[2 * e] = __builtin_bit_cast(uint32_t, b0);
                     o8[2 * e + 1] = __builtin_bit_cast(uint32_t, b1);
                 }
