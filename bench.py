@@ -212,12 +212,15 @@ def time_decode(args, cfg, inp, caches, newest, ds):
 
 def decode_bytes(inp, k, h, kv_row_bytes=1152):
     """Algorithmic HBM bytes per decode step; a latent row is 1152 B in bf16,
-    576 B of codes + a 4-byte scale in FP8."""
+    576 B of codes + a 4-byte scale in FP8.  With several queries per sequence
+    the keys of a sequence count once (the scan they could share)."""
     n_keys = int(inp.lens.sum())
+    n_q = int(inp.q_pos.numel())
+    n_scores = float((inp.q_pos.long() + 1).sum())
     return {
-        "indexer_bytes": n_keys * (128 + 4) + inp.iq.numel() + 4.0 * n_keys,   # keys + scales read, scores written
-        "topk_bytes": 4.0 * n_keys + 4.0 * inp.lens.numel() * k,
-        "mla_bytes": inp.lens.numel() * k * (kv_row_bytes + 4 + 4) + inp.q.numel() * 2 + inp.lens.numel() * h * 512 * 2,
+        "indexer_bytes": n_keys * (128 + 4) + inp.iq.numel() + 4.0 * n_scores,   # keys + scales read, scores written
+        "topk_bytes": 4.0 * n_scores + 4.0 * n_q * k,
+        "mla_bytes": n_q * k * (kv_row_bytes + 4 + 4) + inp.q.numel() * 2 + n_q * h * 512 * 2,
     }
 
 
@@ -331,6 +334,28 @@ def main():
                             "us_per_step": dwall * 1e6, "tokens_per_s": dcfg.decode_batch / dwall,
                             "stages_us": {k2: v * 1e3 for k2, v in dst.items()}, "kernels": dk}
         log(f"[bench] decode {dwall * 1e6:.1f} us/step; stages us {result['decode']['stages_us']}")
+        # multi-token-prediction shape: 2 query tokens per sequence over the same caches
+        iq2, iqs2, w2, q2, pos2, seq2 = synth.decode_queries(dcfg, dinp.lens, 2, dev)
+        dinp2 = dataclasses.replace(dinp, iq=iq2, iq_scale=iqs2, w=w2, q=q2, q_pos=pos2, q_seq=seq2)
+        both = torch.stack([dinp.seq_start + dinp.lens - 2, dinp.seq_start + dinp.lens - 1], 1).reshape(-1).to(dev)
+        newest2 = dict(ik=dinp.ik[both], ik_scale=dinp.ik_scale[both], ik_slot=dinp.ik_slot[both], kv=dinp.kv[both],
+                       kv_slot=kv_slot[both])
+        ds2 = P.alloc_decode(2 * dcfg.decode_batch, int(dinp.lens.max()), dcfg.k, dcfg.h, device=dev)
+        dwall2, dst2 = time_decode(args, dcfg, dinp2, caches, newest2, ds2)
+        db2 = decode_bytes(dinp2, dcfg.k, dcfg.h)
+        dk2 = {name: {"bound": "hbm", "achieved": db2[key] / (dst2[st] * 1e-3) / 1e9, "peak": PEAK_HBM, "unit": "GB/s",
+                      "us": dst2[st] * 1e3} for name, key, st in
+               (("indexer", "indexer_bytes", "indexer"), ("topk", "topk_bytes", "topk"),
+                ("sparse_mla_decode", "mla_bytes", "mla"))}
+        for v in dk2.values():
+            v["frac"] = v["achieved"] / v["peak"]
+        result["decode_mtp2"] = {
+            "workload": "the decode step above with 2 query tokens per sequence (positions N-2, N-1): 128 queries",
+            "us_per_step": dwall2 * 1e6, "tokens_per_s": 2 * dcfg.decode_batch / dwall2,
+            "stages_us": {k2: v * 1e3 for k2, v in dst2.items()}, "kernels": dk2}
+        log(f"[bench] decode, 2 queries per sequence: {dwall2 * 1e6:.1f} us/step; stages us "
+            f"{result['decode_mtp2']['stages_us']}")
+        del ds2, dinp2, q2, iq2
         # the same step over an FP8 E4M3 latent cache (per-token scale)
         caches = fp8_kv_caches(caches, dinp, kv_slot)
         dwall8, dst8 = time_decode(args, dcfg, dinp, caches, newest, ds)

@@ -21,4 +21,4 @@ from .gen import (  # noqa: F401
     gen, normal, bf16_normal, fp8_per_token, randperm, e1_codes, e1_pow2_scales, e1_weights,
     bf16_bits, fp8_bits,
 )
-from .configs import CONFIGS, PrefillInputs, DecodeInputs, make_prefill, make_decode  # noqa: F401
+from .configs import CONFIGS, PrefillInputs, DecodeInputs, make_prefill, make_decode, decode_queries  # noqa: F401

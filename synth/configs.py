@@ -144,15 +144,15 @@ class DecodeInputs:
     cfg: Config
     lens: torch.Tensor        # [B] int64 context length of each sequence (incl. the query token)
     seq_start: torch.Tensor   # [B] int64 first logical row of each sequence in ik / kv
-    iq: torch.Tensor          # [B, H_I, D_I] uint8
-    iq_scale: torch.Tensor    # [B]
-    w: torch.Tensor           # [B, H_I]
+    iq: torch.Tensor          # [B m, H_I, D_I] uint8 (m query tokens per sequence, sequence-major)
+    iq_scale: torch.Tensor    # [B m]
+    w: torch.Tensor           # [B m, H_I]
     ik: torch.Tensor          # [N, D_I] uint8, all sequences concatenated (logical order)
     ik_scale: torch.Tensor    # [N]
-    q: torch.Tensor           # [B, H, 576] bf16
+    q: torch.Tensor           # [B m, H, 576] bf16
     kv: torch.Tensor          # [N, 576] bf16 (logical order)
-    q_pos: torch.Tensor       # [B] int32 = lens - 1
-    q_seq: torch.Tensor       # [B] int32 = arange(B)
+    q_pos: torch.Tensor       # [B m] int32: lens - m .. lens - 1 per sequence
+    q_seq: torch.Tensor       # [B m] int32: b repeated m times
     page_table: torch.Tensor  # [B, max_pages] int32 (-1 past each sequence's last page)
     ik_slot: torch.Tensor     # [N] int64
     kv_slot_table: torch.Tensor  # [B, max_len] int32 (-1 past each sequence's end)
@@ -160,10 +160,27 @@ class DecodeInputs:
     n_slots: int
 
 
-def make_decode(cfg="C4", device="cpu", batch=None, ctx_lo=None, ctx_hi=None):
-    """One decode step: B sequences, one query token each at the last
-    position of its context.  Physical pages / slots of all sequences are one
-    shuffled pool."""
+def decode_queries(cfg, lens, m=1, device="cpu"):
+    """Query-side tensors of a decode step with m query tokens per sequence, at
+    the last m positions of each context (the shape multi-token prediction
+    presents); m = 1 is the plain one-token step.  Returns (iq, iq_scale, w, q,
+    q_pos, q_seq) with rows in sequence-major order."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    B = lens.numel()
+    x = 0 if m == 1 else 10 + m
+    iq, iq_scale = fp8_per_token(normal((B * m, cfg.h_i, cfg.d_i), _seed(cfg, T_IQ, x), device))
+    w = normal((B * m, cfg.h_i), _seed(cfg, T_W, x), device, std=(1.0 / cfg.h_i) ** 0.5)
+    q = bf16_normal((B * m, cfg.h, DK), _seed(cfg, T_Q, x), device)
+    q_pos = (lens.cpu().view(-1, 1) - m + torch.arange(m).view(1, -1)).reshape(-1).to(torch.int32)
+    q_seq = torch.arange(B, dtype=torch.int32).repeat_interleave(m)
+    return iq, iq_scale, w, q, q_pos.to(device), q_seq.to(device)
+
+
+def make_decode(cfg="C4", device="cpu", batch=None, ctx_lo=None, ctx_hi=None, queries_per_seq=1):
+    """One decode step: B sequences, `queries_per_seq` query tokens each at the
+    last positions of its context (default one).  Physical pages / slots of all
+    sequences are one shuffled pool."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     B = batch or cfg.decode_batch
@@ -189,13 +206,10 @@ def make_decode(cfg="C4", device="cpu", batch=None, ctx_lo=None, ctx_hi=None):
         ik_slot[seq_start[b]:seq_start[b] + nb] = page_table[b].to(torch.int64)[s // PAGE] * PAGE + s % PAGE
         kv_slot_table[b, :nb] = slot_perm[seq_start[b]:seq_start[b] + nb]
         p0 += npg
-    iq, iq_scale = fp8_per_token(normal((B, cfg.h_i, cfg.d_i), _seed(cfg, T_IQ), device))
-    w = normal((B, cfg.h_i), _seed(cfg, T_W), device, std=(1.0 / cfg.h_i) ** 0.5)
+    iq, iq_scale, w, q, q_pos, q_seq = decode_queries(cfg, lens, queries_per_seq, device)
     ik, ik_scale = fp8_per_token(normal((N, cfg.d_i), _seed(cfg, T_IK), device))
-    q = bf16_normal((B, cfg.h, DK), _seed(cfg, T_Q), device)
     kv = bf16_normal((N, DK), _seed(cfg, T_KV), device)
     return DecodeInputs(cfg=cfg, lens=lens, seq_start=seq_start, iq=iq, iq_scale=iq_scale, w=w, ik=ik,
-                        ik_scale=ik_scale, q=q, kv=kv, q_pos=(lens - 1).to(torch.int32).to(device),
-                        q_seq=torch.arange(B, dtype=torch.int32, device=device),
+                        ik_scale=ik_scale, q=q, kv=kv, q_pos=q_pos, q_seq=q_seq,
                         page_table=page_table.to(device), ik_slot=ik_slot.to(device),
                         kv_slot_table=kv_slot_table.to(device), n_pages=n_pages, n_slots=N)

@@ -335,13 +335,15 @@ def test_chunked_equals_monolithic():
 
 
 # ------------------------------------------------------------------ decode
-@pytest.mark.parametrize("batch,lo,hi,n_splits,kv_fp8", [(8, 2000, 9000, 0, False), (5, 100, 3000, 3, False),
-                                                         (3, 2049, 2049, 1, False), (6, 1500, 7000, 0, True),
-                                                         (4, 2049, 4100, 2, True)])
-def test_decode_vs_oracle(batch, lo, hi, n_splits, kv_fp8):
-    say(f"[decode] B={batch} ctx=[{lo},{hi}] splits={n_splits} fp8={kv_fp8}")
+@pytest.mark.parametrize("batch,lo,hi,n_splits,kv_fp8,m", [(8, 2000, 9000, 0, False, 1), (5, 100, 3000, 3, False, 1),
+                                                           (3, 2049, 2049, 1, False, 1), (6, 1500, 7000, 0, True, 1),
+                                                           (4, 2049, 4100, 2, True, 1), (5, 1900, 6000, 0, False, 3),
+                                                           (4, 2050, 2052, 2, True, 2)])
+def test_decode_vs_oracle(batch, lo, hi, n_splits, kv_fp8, m):
+    """m query tokens per sequence (m > 1: the multi-token-prediction shape)."""
+    say(f"[decode] B={batch} ctx=[{lo},{hi}] splits={n_splits} fp8={kv_fp8} queries/seq={m}")
     c = CONFIGS["C4"]
-    inp = synth.make_decode(c, batch=batch, ctx_lo=lo, ctx_hi=hi)
+    inp = synth.make_decode(c, batch=batch, ctx_lo=lo, ctx_hi=hi, queries_per_seq=m)
     d = lambda x: x.to(DEV)
     caches = P.alloc_prefill(inp.n_pages, c.d_i, inp.n_slots, 1, 1, c.k, c.h, kv_fp8=kv_fp8)
     kv_slot = torch.empty(inp.n_slots, dtype=torch.int64)
@@ -350,7 +352,7 @@ def test_decode_vs_oracle(batch, lo, hi, n_splits, kv_fp8):
         kv_slot[s0:s0 + nb] = inp.kv_slot_table[b, :nb].long()
     P.store_tokens(caches, d(inp.ik), d(inp.ik_scale), d(inp.ik_slot), d(inp.kv), d(kv_slot))
     ld = int(inp.lens.max())
-    ds = P.alloc_decode(batch, ld, c.k, c.h, n_splits=n_splits)
+    ds = P.alloc_decode(batch * m, ld, c.k, c.h, n_splits=n_splits)
     P.decode_step(ds, caches, d(inp.iq), d(inp.iq_scale), d(inp.w), d(inp.page_table), d(inp.kv_slot_table),
                   d(inp.q_seq), d(inp.q_pos), d(inp.q), c.k, SM_SCALE)
     torch.cuda.synchronize()
@@ -360,11 +362,12 @@ def test_decode_vs_oracle(batch, lo, hi, n_splits, kv_fp8):
                                 pos, seq_start=inp.seq_start.numpy(), q_seq=inp.q_seq.numpy(), ld=ld,
                                 n_threads=oracle_threads())
     mask = np.arange(ld)[None, :] <= pos[:, None]
-    for b in range(batch):
-        s0, nb = int(inp.seq_start[b]), int(inp.lens[b])
-        A = indexer_abs_scale(inp.iq[b:b + 1], inp.iq_scale[b:b + 1], inp.w[b:b + 1], inp.ik[s0:s0 + nb],
-                              inp.ik_scale[s0:s0 + nb], np.arange(1))
-        assert (np.abs(g[b, :nb] - ref[b, :nb]) <= BOUND_C * A[0] + 1e-30).all(), b
+    for t in range(batch * m):
+        b = int(inp.q_seq[t])
+        s0, nk = int(inp.seq_start[b]), int(pos[t]) + 1
+        A = indexer_abs_scale(inp.iq[t:t + 1], inp.iq_scale[t:t + 1], inp.w[t:t + 1], inp.ik[s0:s0 + nk],
+                              inp.ik_scale[s0:s0 + nk], np.arange(1))
+        assert (np.abs(g[t, :nk] - ref[t, :nk]) <= BOUND_C * A[0] + 1e-30).all(), t
     np.testing.assert_array_equal(ds.idx.cpu().numpy(), oracle.topk(g, pos, c.k))
     idx = ds.idx.cpu().numpy()
     if kv_fp8:
