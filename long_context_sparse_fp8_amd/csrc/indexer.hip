@@ -227,17 +227,18 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 constexpr int kWavePages = 16;                    // page slots per wave (4 waves: 64 pages per split)
 constexpr int kDecDepth = 1;                      // pages per wave in flight while one is scored
 
-// Workgroup = one query x a range of at most 64 key pages; the 4 waves take
-// pages round-robin and load B fragments straight from the cache (each key
-// byte is used by exactly one query, so there is nothing to share through
-// LDS).  The query's A fragments and head weights are staged in LDS (shared by
-// the 4 waves; 64 fewer registers per wave), every wave keeps kDecDepth page(s)
-// in flight while it scores one, and the split's page-table entries are read
-// once up front (lane i holds page p_begin + i, broadcast with a lane read), so
-// no key load waits on a table load.  A wave's scores stay in registers and are
-// stored after its last page: stores and loads share one completion counter,
-// so a store between the page loads would make every later wait also wait for
-// it (measured: 20% of the scan).
+// Workgroup = query t x a range of at most 64 key pages; the 4 waves take
+// pages round-robin and load B fragments straight from the cache.  Queries
+// 2i and 2i + 1 of one sequence (several query tokens per sequence, as
+// multi-token prediction presents them) are scored together: each page is
+// loaded once for both, the pair's two workgroups taking half the range each.  The queries' A fragments and head weights are staged in LDS
+// (shared by the 4 waves) and read from there for every page; every wave keeps
+// kDecDepth page(s) in flight while it scores one, and the split's page-table
+// entries are read once up front (lane i holds page p_begin + i, broadcast
+// with a lane read), so no key load waits on a table load.  A wave's scores
+// stay in registers and are stored after its last page: stores and loads share
+// one completion counter, so a store between the page loads would make every
+// later wait also wait for it (measured: 20% of the scan).
 template <int H_I, int D_I>
 __global__ __launch_bounds__(256, 2) void indexer_decode_kernel(
     const uint8_t *__restrict__ q_fp8, const float *__restrict__ q_scale, const float *__restrict__ w, int64_t w_ld,
@@ -246,128 +247,158 @@ __global__ __launch_bounds__(256, 2) void indexer_decode_kernel(
     const int32_t *__restrict__ q_pos, int32_t n_q, float *__restrict__ scores, int64_t ld, int pages_per_split) {
     using S = IdxShape<H_I, D_I>;
     constexpr int NH = 32 * S::HT;                   // heads rounded up to MFMA row tiles
-    __shared__ __attribute__((aligned(16))) uint8_t q_lds[NH * S::ROW];   // padded rows: conflict-free reads
-    __shared__ __attribute__((aligned(16))) float w_lds[NH];
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[2][NH * S::ROW];   // padded rows: conflict-free reads
+    __shared__ __attribute__((aligned(16))) float w_lds[2][NH];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
     const int t = blockIdx.x;
-    const int pos = q_pos[t];
-    int64_t n_pg = pos < 0 ? 0 : (int64_t)pos / kPage + 1;
     const int64_t max_page = (ld + kPage - 1) / kPage;
-    if (n_pg > max_page) n_pg = max_page;
-    const int64_t p_begin = (int64_t)blockIdx.y * pages_per_split;
-    const int64_t p_end = min(n_pg, p_begin + pages_per_split);   // pages_per_split <= 4 kWavePages
-    if (p_begin >= p_end) return;                    // uniform over the workgroup
-    if (n_pages <= 0) {                                  // no page can be read: every score is NaN
-        for (int64_t key = p_begin * kPage + threadIdx.x; key < min(p_end * kPage, min((int64_t)pos + 1, ld));
-             key += 256)
-            scores[(int64_t)t * ld + key] = __builtin_nanf("");
-        return;
-    }
 
-    // physical page of page p_begin + lane, -1 when absent or out of range
-    int32_t my_phys = -1;
-    {
-        const int32_t *pt_row = page_table + (int64_t)q_seq[t] * pt_ld;
-        const int64_t pp = p_begin + lane;
-        if (pp < p_end && pp < pt_ld) {
-            const int32_t v = pt_row[pp];
-            if (v >= 0 && v < n_pages) my_phys = v;
+    // Score queries t1 .. t1 + NQ - 1 (one sequence) against pages p_begin ..
+    // p_begin + 4 SLOTS - 1 (at most 64: one page-table entry per lane).
+    auto run = [&](auto nq_c, auto slots_c, const int t1, const int64_t p_begin) {
+        constexpr int NQ = decltype(nq_c)::value, SLOTS = decltype(slots_c)::value;
+        static_assert(4 * SLOTS <= 64, "one page-table entry per lane");
+        int pos[NQ], pmax = -1;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            pos[j] = q_pos[t1 + j];
+            pmax = max(pmax, pos[j]);
         }
-    }
-    // the query's FP8 rows (heads past H_I zero) and weights, once per workgroup
-    for (int c = threadIdx.x; c < NH * S::CH; c += 256) {
-        const int head = c / S::CH, col = c % S::CH;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (head < H_I) v = reinterpret_cast<const uint4 *>(q_fp8 + ((int64_t)t * H_I + head) * D_I)[col];
-        *reinterpret_cast<uint4 *>(&q_lds[head * S::ROW + col * 16]) = v;
-    }
-    for (int hh = threadIdx.x; hh < NH; hh += 256) w_lds[hh] = hh < H_I ? w[(int64_t)t * w_ld + hh] : 0.0f;
-    const float qs = q_scale[t];
-    __syncthreads();
+        int64_t n_pg = pmax < 0 ? 0 : (int64_t)pmax / kPage + 1;
+        if (n_pg > max_page) n_pg = max_page;
+        const int64_t p_end = min(n_pg, p_begin + 4 * SLOTS);
+        if (p_begin >= p_end) return;                // uniform over the workgroup
+        if (n_pages <= 0) {                          // no page can be read: every score is NaN
+#pragma unroll
+            for (int j = 0; j < NQ; ++j)
+                for (int64_t key = p_begin * kPage + threadIdx.x;
+                     key < min(p_end * kPage, min((int64_t)pos[j] + 1, ld)); key += 256)
+                    scores[(int64_t)(t1 + j) * ld + key] = __builtin_nanf("");
+            return;
+        }
+        // physical page of page p_begin + lane, -1 when absent or out of range
+        int32_t my_phys = -1;
+        {
+            const int32_t *pt_row = page_table + (int64_t)q_seq[t1] * pt_ld;
+            const int64_t pp = p_begin + lane;
+            if (pp < p_end && pp < pt_ld) {
+                const int32_t v = pt_row[pp];
+                if (v >= 0 && v < n_pages) my_phys = v;
+            }
+        }
+        // the queries' FP8 rows (heads past H_I zero) and weights
+        __syncthreads();                             // a previous run's readers are done
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            for (int c = threadIdx.x; c < NH * S::CH; c += 256) {
+                const int head = c / S::CH, col = c % S::CH;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (head < H_I) v = reinterpret_cast<const uint4 *>(q_fp8 + ((int64_t)(t1 + j) * H_I + head) * D_I)[col];
+                *reinterpret_cast<uint4 *>(&q_lds[j][head * S::ROW + col * 16]) = v;
+            }
+            for (int hh = threadIdx.x; hh < NH; hh += 256) w_lds[j][hh] = hh < H_I ? w[(int64_t)(t1 + j) * w_ld + hh] : 0.0f;
+        }
+        float qs[NQ];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) qs[j] = q_scale[t1 + j];
+        __syncthreads();
 
-    // Score of key `lane` of a page whose B fragments are in `b` (same mapping
-    // as page_scores, with A fragments and weights read from LDS).
-    auto scores_of = [&](const i32x8 (&b)[2][S::KC]) -> float {
-        float part[2];
+        // Score of key `lane` of a page whose B fragments are in `b` for query j
+        // (same mapping as the prefill scorer, with A fragments and weights
+        // read from LDS for every page).
+        auto scores_of = [&](const i32x8 (&b)[2][S::KC], const int j) -> float {
+            asm volatile("" ::: "memory");           // q and w come from LDS, not kept in registers
+            float part[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            f32x16 acc[S::HT];
+            for (int kt = 0; kt < 2; ++kt) {
+                f32x16 acc[S::HT];
 #pragma unroll
-            for (int ht = 0; ht < S::HT; ++ht) {
-                acc[ht] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-                const uint8_t *qrow = &q_lds[(32 * ht + (lane & 31)) * S::ROW + g * S::HALF];
+                for (int ht = 0; ht < S::HT; ++ht) {
+                    acc[ht] = f32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                    const uint8_t *qrow = &q_lds[j][(32 * ht + (lane & 31)) * S::ROW + g * S::HALF];
+#pragma unroll
+                    for (int c = 0; c < S::KC; ++c) {
+                        const uint4 lo = *reinterpret_cast<const uint4 *>(qrow + 32 * c);
+                        const uint4 hi = *reinterpret_cast<const uint4 *>(qrow + 32 * c + 16);
+                        const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        acc[ht] = mfma_f8_32x32x64(a, b[kt][c], acc[ht]);
+                    }
+                }
+                float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+                for (int ht = 0; ht < S::HT; ++ht) {
+#pragma unroll
+                    for (int i = 0; i < 16; i += 4) {
+                        // accumulator element i: head 32 ht + 8 (i / 4) + 4 g + i % 4
+                        const float4 wv = *reinterpret_cast<const float4 *>(&w_lds[j][32 * ht + 2 * i + 4 * g]);
+                        s0 = fmaf(wv.x, relu_bits(acc[ht][i + 0]), s0);
+                        s1 = fmaf(wv.y, relu_bits(acc[ht][i + 1]), s1);
+                        s2 = fmaf(wv.z, relu_bits(acc[ht][i + 2]), s2);
+                        s3 = fmaf(wv.w, relu_bits(acc[ht][i + 3]), s3);
+                    }
+                }
+                part[kt] = (s0 + s1) + (s2 + s3);
+            }
+            // lane i < 32: key i (tile 0); lane 32 + i: key 32 + i (tile 1)
+            return halves_reduce_scatter(part[0], part[1]);
+        };
+
+        // Page slot m of this wave is page p_begin + wave + 4 m.  Every wave runs all
+        // SLOTS slots, fully unrolled and branch-free: a slot past the split
+        // loads a page of the split again and stores nothing.  With no loop back-edge
+        // the compiler can wait for exactly the page being scored while the next ones
+        // stay in flight.
+        auto fetch = [&](int m, i32x8 (&b)[2][S::KC], float &ksc) {
+            const int64_t p = min(p_begin + wave + 4 * m, p_end - 1);
+            const int32_t phys0 = __builtin_amdgcn_readlane(my_phys, (int)(p - p_begin));
+            const int32_t phys = phys0 < 0 ? 0 : phys0;      // absent page: scores become NaN below
+            const uint8_t *base = key_cache + (int64_t)phys * (kPage * D_I);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
                 for (int c = 0; c < S::KC; ++c) {
-                    const uint4 lo = *reinterpret_cast<const uint4 *>(qrow + 32 * c);
-                    const uint4 hi = *reinterpret_cast<const uint4 *>(qrow + 32 * c + 16);
-                    const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    acc[ht] = mfma_f8_32x32x64(a, b[kt][c], acc[ht]);
+                    const uint4 *src = reinterpret_cast<const uint4 *>(base + (kt * S::KC + c) * 2048 + 16 * lane);
+                    const uint4 lo = src[0], hi = src[64];   // blocks h = 0, 1: one contiguous 1 KB load each
+                    b[kt][c] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 }
             }
-            float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+            const float k = key_scale[(int64_t)phys * kPage + lane];
+            ksc = phys0 < 0 ? __builtin_nanf("") : k;
+        };
+        float sreg[NQ][SLOTS];
+        constexpr int D = kDecDepth + 1;             // ring slots: in flight + the one scored
+        i32x8 bf[D][2][S::KC];
+        float kf[D];
 #pragma unroll
-            for (int ht = 0; ht < S::HT; ++ht) {
+        for (int m = 0; m < kDecDepth; ++m) fetch(m, bf[m], kf[m]);
 #pragma unroll
-                for (int i = 0; i < 16; i += 4) {
-                    // accumulator element i: head 32 ht + 8 (i / 4) + 4 g + i % 4
-                    const float4 wv = *reinterpret_cast<const float4 *>(&w_lds[32 * ht + 2 * i + 4 * g]);
-                    s0 = fmaf(wv.x, relu_bits(acc[ht][i + 0]), s0);
-                    s1 = fmaf(wv.y, relu_bits(acc[ht][i + 1]), s1);
-                    s2 = fmaf(wv.z, relu_bits(acc[ht][i + 2]), s2);
-                    s3 = fmaf(wv.w, relu_bits(acc[ht][i + 3]), s3);
-                }
-            }
-            part[kt] = (s0 + s1) + (s2 + s3);
+        for (int m = 0; m < SLOTS; ++m) {
+            if (m + kDecDepth < SLOTS) fetch(m + kDecDepth, bf[(m + kDecDepth) % D], kf[(m + kDecDepth) % D]);
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) sreg[j][m] = scores_of(bf[m % D], j) * (qs[j] * kf[m % D]);
         }
-        // lane i < 32: key i (tile 0); lane 32 + i: key 32 + i (tile 1)
-        return halves_reduce_scatter(part[0], part[1]);
-    };
-
-    // Page slot m of this wave is page p_begin + wave + 4 m.  Every wave runs all
-    // kWavePages slots, fully unrolled and branch-free: a slot past the split
-    // loads a page of the split again and stores nothing.  With no loop back-edge
-    // the compiler can wait for exactly the page being scored while the next ones
-    // stay in flight.
-    auto fetch = [&](int m, i32x8 (&b)[2][S::KC], float &ksc) {
-        const int64_t p = min(p_begin + wave + 4 * m, p_end - 1);
-        const int32_t phys0 = __builtin_amdgcn_readlane(my_phys, (int)(p - p_begin));
-        const int32_t phys = phys0 < 0 ? 0 : phys0;      // absent page: scores become NaN below
-        const uint8_t *base = key_cache + (int64_t)phys * (kPage * D_I);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int j = 0; j < NQ; ++j) {
+            const int64_t k_end = min(p_end * kPage, min((int64_t)pos[j] + 1, ld));
+            float *srow = scores + (int64_t)(t1 + j) * ld;
 #pragma unroll
-            for (int c = 0; c < S::KC; ++c) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(base + (kt * S::KC + c) * 2048 + 16 * lane);
-                const uint4 lo = src[0], hi = src[64];   // blocks h = 0, 1: one contiguous 1 KB load each
-                b[kt][c] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            for (int m = 0; m < SLOTS; ++m) {
+                const int64_t key = (p_begin + wave + 4 * m) * kPage + lane;
+                if (key < k_end) srow[key] = sreg[j][m];
             }
         }
-        const float k = key_scale[(int64_t)phys * kPage + lane];
-        ksc = phys0 < 0 ? __builtin_nanf("") : k;
-    };
-    float sreg[kWavePages];
-    auto score = [&](int m, const i32x8 (&b)[2][S::KC], float ksc) {
-        const float sc = scores_of(b);
-        sreg[m] = sc * (qs * ksc);
     };
 
-    constexpr int D = kDecDepth + 1;                 // ring slots: in flight + the one scored
-    i32x8 bf[D][2][S::KC];
-    float kf[D];
-#pragma unroll
-    for (int m = 0; m < kDecDepth; ++m) fetch(m, bf[m], kf[m]);
-#pragma unroll
-    for (int m = 0; m < kWavePages; ++m) {
-        if (m + kDecDepth < kWavePages) fetch(m + kDecDepth, bf[(m + kDecDepth) % D], kf[(m + kDecDepth) % D]);
-        score(m, bf[m % D], kf[m % D]);
-    }
-    const int64_t k_end = min(p_end * kPage, min((int64_t)pos + 1, ld));
-    float *srow = scores + (int64_t)t * ld;
-#pragma unroll
-    for (int m = 0; m < kWavePages; ++m) {
-        const int64_t key = (p_begin + wave + 4 * m) * kPage + lane;
-        if (key < k_end) srow[key] = sreg[m];
-    }
+    // Queries 2i, 2i + 1 of one sequence: the two workgroups of a split score
+    // both queries, each over half of the split's pages.  The decision is
+    // uniform over the workgroup.
+    const int64_t p_split = (int64_t)blockIdx.y * pages_per_split;   // pages_per_split = 4 kWavePages
+    const int partner = t ^ 1;
+    if (partner < n_q && q_seq[partner] == q_seq[t])
+        run(std::integral_constant<int, 2>{}, std::integral_constant<int, kWavePages / 2>{}, t & ~1,
+            p_split + (t & 1) * (2 * kWavePages));
+    else
+        run(std::integral_constant<int, 1>{}, std::integral_constant<int, kWavePages>{}, t, p_split);
 }
 
 // ------------------------------------------------------------------ launch
