@@ -210,6 +210,34 @@ def time_decode(args, cfg, inp, caches, newest, ds):
     return (time.perf_counter() - t0) / args.steps, timer.avg_ms()
 
 
+def time_decode_graph(args, cfg, inp, caches, newest, ds):
+    """The decode step captured once as a HIP graph (the 7 launches of the step in
+    one submission, as a serving loop would run it) and replayed: (seconds per
+    step, whether the replayed outputs equal the eager ones bit for bit)."""
+    run_decode_step(cfg, inp, caches, newest, ds)
+    torch.cuda.synchronize()
+    ref = (ds.idx.clone(), ds.out.clone(), ds.lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_decode_step(cfg, inp, caches, newest, ds)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_decode_step(cfg, inp, caches, newest, ds)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(ref, (ds.idx, ds.out, ds.lse)))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    del graph
+    return wall, same
+
+
 def decode_bytes(inp, k, h, kv_row_bytes=1152):
     """Algorithmic HBM bytes per decode step; a latent row is 1152 B in bf16,
     576 B of codes + a 4-byte scale in FP8.  With several queries per sequence
@@ -334,6 +362,10 @@ def main():
                             "us_per_step": dwall * 1e6, "tokens_per_s": dcfg.decode_batch / dwall,
                             "stages_us": {k2: v * 1e3 for k2, v in dst.items()}, "kernels": dk}
         log(f"[bench] decode {dwall * 1e6:.1f} us/step; stages us {result['decode']['stages_us']}")
+        gwall, gsame = time_decode_graph(args, dcfg, dinp, caches, newest, ds)
+        result["decode"]["us_per_step_graph"] = gwall * 1e6
+        result["decode"]["graph_replay_matches_eager"] = gsame
+        log(f"[bench] decode as a replayed graph {gwall * 1e6:.1f} us/step (outputs equal to eager: {gsame})")
         # multi-token-prediction shape: 2 query tokens per sequence over the same caches
         iq2, iqs2, w2, q2, pos2, seq2 = synth.decode_queries(dcfg, dinp.lens, 2, dev)
         dinp2 = dataclasses.replace(dinp, iq=iq2, iq_scale=iqs2, w=w2, q=q2, q_pos=pos2, q_seq=seq2)

@@ -407,3 +407,47 @@ def test_decode_row_matches_prefill_row():
     assert torch.equal(ds.scores[0, :L], st.scores[L - 1])      # same per-pair arithmetic in both indexers
     assert torch.equal(ds.idx[0], st.idx[L - 1])
     assert max_abs_rel(ds.out[0].float().cpu().numpy(), st.out[L - 1].float().cpu().numpy()) <= 1e-2
+
+
+def test_decode_graph_replay_matches_eager():
+    """The decode step captured as a HIP graph replays to the eager result, bit for bit,
+    on every replay (eager work and synchronizations between the replays)."""
+    say("[graph] decode step captured and replayed")
+    c = CONFIGS["C4"]
+    inp = synth.make_decode(c, batch=6, ctx_lo=2100, ctx_hi=7000, queries_per_seq=2)
+    d = lambda x: x.to(DEV)
+    caches = P.alloc_prefill(inp.n_pages, c.d_i, inp.n_slots, 1, 1, c.k, c.h)
+    kv_slot = torch.empty(inp.n_slots, dtype=torch.int64)
+    for b in range(6):
+        s0, nb = int(inp.seq_start[b]), int(inp.lens[b])
+        kv_slot[s0:s0 + nb] = inp.kv_slot_table[b, :nb].long()
+    P.store_tokens(caches, d(inp.ik), d(inp.ik_scale), d(inp.ik_slot), d(inp.kv), d(kv_slot))
+    args = [d(inp.iq), d(inp.iq_scale), d(inp.w), d(inp.page_table), d(inp.kv_slot_table), d(inp.q_seq),
+            d(inp.q_pos), d(inp.q)]
+    ld = int(inp.lens.max())
+    ds = P.alloc_decode(12, ld, c.k, c.h)
+    step = lambda st: P.decode_step(st, caches, *args, c.k, SM_SCALE)
+    step(ds)
+    torch.cuda.synchronize()
+    ref = [ds.idx.clone(), ds.out.clone(), ds.lse.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(ds)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(ds)
+    other = P.alloc_decode(12, ld, c.k, c.h)
+    for r in range(3):
+        ds.idx.fill_(-7)
+        ds.out.zero_()
+        ds.lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        step(other)                      # eager work between the replays
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (ds.idx, ds.out, ds.lse)):
+            assert torch.equal(a, b), r
+        for a, b in zip(ref, (other.idx, other.out, other.lse)):
+            assert torch.equal(a, b), r
