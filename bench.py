@@ -83,6 +83,41 @@ def calib_copy(dev, nbytes=1 << 30, reps=3):
     log(f"[bench] calibration copy: {reps} x {nbytes} bytes")
 
 
+def measured_copy_bandwidth(dev, nbytes=1 << 30, reps=10):
+    """Bytes moved (read + write) per second by a plain 1 GiB device-to-device
+    copy: the HBM bandwidth a streaming kernel reaches on this machine, beside the
+    8 TB/s datasheet peak the roofline fractions use."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def measured_bf16_gemm(dev, n=8192, reps=10):
+    """TFLOP/s of torch's dense bf16 matmul (the vendor GEMM) at n x n x n: what a
+    library GEMM reaches on this machine, beside the 2.5 PFLOP/s datasheet peak."""
+    a = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    del c
+    return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -406,6 +441,10 @@ def main():
 
     if args.calib_copy:
         calib_copy(dev)
+    result["measured_peaks"] = {"hbm_copy_GBps": measured_copy_bandwidth(dev),
+                                "bf16_gemm_TFLOPs": measured_bf16_gemm(dev),
+                                "note": "1 GiB device-to-device copy (read + write bytes per second); torch bf16 "
+                                        "matmul 8192^3"}
 
     # ---- CPU baseline (the oracle on a bounded sample)
     if not args.no_cpu:
