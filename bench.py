@@ -118,6 +118,27 @@ def measured_bf16_gemm(dev, n=8192, reps=10):
     return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
+def measured_fp8_gemm(dev, n=8192, reps=10):
+    """TFLOP/s of torch's FP8 (E4M3) scaled matmul at n x n x n, or None where
+    this torch build has no FP8 GEMM for the device."""
+    try:
+        a = torch.randn((n, n), device=dev).to(torch.float8_e4m3fn)
+        b = torch.randn((n, n), device=dev).to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device=dev)
+        mm = lambda: torch._scaled_mm(a, b, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        mm()
+        torch.cuda.synchronize()
+    except (RuntimeError, TypeError, AttributeError):
+        return None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mm()
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -443,8 +464,9 @@ def main():
         calib_copy(dev)
     result["measured_peaks"] = {"hbm_copy_GBps": measured_copy_bandwidth(dev),
                                 "bf16_gemm_TFLOPs": measured_bf16_gemm(dev),
+                                "fp8_gemm_TFLOPs": measured_fp8_gemm(dev),
                                 "note": "1 GiB device-to-device copy (read + write bytes per second); torch bf16 "
-                                        "matmul 8192^3"}
+                                        "matmul and FP8 E4M3 scaled matmul at 8192^3"}
 
     # ---- CPU baseline (the oracle on a bounded sample)
     if not args.no_cpu:
