@@ -23,7 +23,7 @@ are unchanged, otherwise as null.  --calib-copy adds one plain 1 GiB
 device-to-device copy after the timed work, the known-size kernel those
 counter runs are scaled by.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--calib-copy]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--calib-copy] [--configs]
 """
 import argparse
 import dataclasses
@@ -329,6 +329,161 @@ def cpu_baseline(inp, cfg, n_rows):
                       f"indexer row + top-k + sparse MLA each, {dt:.1f} s wall on {threads} threads"}
 
 
+# ---------------------------------------------------------------------------- all configs
+def oracle_prefill_rate(inp, cfg, rows, ld):
+    """Oracle tokens/s over the given query rows of a prefill input (full indexer
+    row + top-k + sparse MLA each)."""
+    import oracle
+    u8 = lambda t: t.detach().cpu().contiguous().numpy().view(np.uint8)
+    b16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    rows = np.asarray(rows, dtype=np.int64)
+    iq, iqs, w = u8(inp.iq[rows]), inp.iq_scale[rows].cpu().numpy(), inp.w[rows].cpu().numpy()
+    ik, iks = u8(inp.ik), inp.ik_scale.cpu().numpy()
+    q = inp.q[rows] if inp.q is not None else torch.cat([inp.q_chunk(int(r), int(r) + 1) for r in rows])
+    kv = b16(inp.kv)
+    pos = inp.q_pos[rows].cpu().numpy().astype(np.int32)
+    threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    sc = oracle.indexer_scores(iq, iqs, w, ik, iks, pos, ld=ld, n_threads=threads)
+    idx = oracle.topk(sc, pos, cfg.k, n_threads=threads)
+    if cfg.kv_fp8:
+        codes, scales = oracle.kv_quantize(kv)
+        oracle.sparse_mla(b16(q), codes, idx, SM_SCALE, kv_scale=scales, n_threads=threads)
+    else:
+        oracle.sparse_mla(b16(q), kv, idx, SM_SCALE, n_threads=threads)
+    dt = time.perf_counter() - t0
+    return {"tokens_per_s": len(rows) / dt, "rows": int(len(rows)), "seconds": dt, "cores": threads}
+
+
+def oracle_decode_rate(inp, cfg, n_seq):
+    """Oracle time of one decode query (indexer over its whole context, top-k,
+    sparse MLA) on the first n_seq sequences, scaled to a step of all of them."""
+    import oracle
+    u8 = lambda t: t.detach().cpu().contiguous().numpy().view(np.uint8)
+    b16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    n_keys = int(inp.lens[:n_seq].sum())
+    pos = inp.q_pos[:n_seq].cpu().numpy().astype(np.int32)
+    seq_start = inp.seq_start[:n_seq].numpy()
+    q_seq = inp.q_seq[:n_seq].cpu().numpy()
+    threads = os.cpu_count() or 1
+    ik, iks, kv = u8(inp.ik[:n_keys]), inp.ik_scale[:n_keys].cpu().numpy(), b16(inp.kv[:n_keys])
+    t0 = time.perf_counter()
+    sc = oracle.indexer_scores(u8(inp.iq[:n_seq]), inp.iq_scale[:n_seq].cpu().numpy(), inp.w[:n_seq].cpu().numpy(),
+                               ik, iks, pos, seq_start=seq_start, q_seq=q_seq, ld=int(inp.lens.max()),
+                               n_threads=threads)
+    idx = oracle.topk(sc, pos, cfg.k, n_threads=threads)
+    oracle.sparse_mla(b16(inp.q[:n_seq]), kv, idx, SM_SCALE, seq_start=seq_start, q_seq=q_seq, n_threads=threads)
+    dt = time.perf_counter() - t0
+    n_all = int(inp.q_pos.numel())
+    return {"us_per_step": dt / n_seq * n_all * 1e6, "queries_timed": n_seq, "seconds": dt, "cores": threads}
+
+
+def sweep_prefill(name, dev, reps=3, oracle_rows=None):
+    """One-pass prefill of config `name` (C1-C3): stage times and rates."""
+    cfg = CONFIGS[name]
+    inp = synth.make_prefill(cfg, device=dev)
+    st = P.alloc_prefill(inp.n_pages, cfg.d_i, inp.n_slots, cfg.L, cfg.L, cfg.k, cfg.h, device=dev)
+    kv_slot = inp.kv_slot_table[0].long()
+    run_prefill_step(cfg, inp, st, kv_slot)
+    torch.cuda.synchronize()
+    timer = StageTimer(["store", "indexer", "topk", "mla"])
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run_prefill_step(cfg, inp, st, kv_slot, timer)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    stg = timer.avg_ms()
+    w = prefill_work(cfg.L, cfg.k, cfg.h_i, cfg.d_i, cfg.h)
+    out = {"L": cfg.L, "k": cfg.k, "indexer": f"{cfg.h_i}x{cfg.d_i}", "mla_heads": cfg.h, "ms_per_pass": wall * 1e3,
+           "tokens_per_s": cfg.L / wall, "stages_ms": stg,
+           "indexer_frac_fp8": w["indexer_flops"] / (stg["indexer"] * 1e-3) / 1e12 / PEAK_FP8,
+           "topk_GBps": w["topk_bytes"] / (stg["topk"] * 1e-3) / 1e9,
+           "mla_frac_bf16": w["mla_flops"] / (stg["mla"] * 1e-3) / 1e12 / PEAK_BF16}
+    if oracle_rows:
+        rows = np.linspace(0, cfg.L - 1, min(oracle_rows, cfg.L)).round().astype(np.int64)
+        out["oracle"] = oracle_prefill_rate(inp, cfg, rows, cfg.L)
+    del st, inp
+    torch.cuda.empty_cache()
+    return out
+
+
+def sweep_chunked(dev, oracle_rows=64):
+    """C5: one 131072-token sequence in 8192-token chunks against its growing
+    prefix, FP8 latent cache: per-chunk stage times, totals and the oracle on a
+    sample of rows."""
+    cfg = CONFIGS["C5"]
+    L, C, k = cfg.L, cfg.chunk, cfg.k
+    inp = synth.make_prefill(cfg, device=dev, materialize_q=False)
+    st = P.alloc_prefill(inp.n_pages, cfg.d_i, inp.n_slots, C, L, k, cfg.h, kv_fp8=True, device=dev)
+    kv_slot = inp.kv_slot_table[0].long()
+    chunks = []
+    t_all = time.perf_counter()
+    for c0 in range(0, L, C):
+        c1 = c0 + C
+        q = inp.q_chunk(c0, c1)
+        torch.cuda.synchronize()
+        timer = StageTimer(["store", "indexer", "topk", "mla"])
+        t0 = time.perf_counter()
+        e = timer.mark("store")
+        P.store_tokens(st, inp.ik[c0:c1], inp.ik_scale[c0:c1], inp.ik_slot[c0:c1], inp.kv[c0:c1], kv_slot[c0:c1])
+        e.record()
+        e = timer.mark("indexer")
+        dsa.indexer_scores(inp.iq[c0:c1], inp.iq_scale[c0:c1], inp.w[c0:c1], st.key_cache, st.key_scale,
+                           inp.page_table, inp.q_seq[c0:c1], inp.q_pos[c0:c1], st.scores)
+        e.record()
+        e = timer.mark("topk")
+        dsa.topk(st.scores, inp.q_pos[c0:c1], k, st.idx)
+        e.record()
+        e = timer.mark("mla")
+        dsa.sparse_mla_prefill(q, st.kv_cache, inp.kv_slot_table, inp.q_seq[c0:c1], st.idx, SM_SCALE, st.out,
+                               st.lse, kv_scale=st.kv_scale)
+        e.record()
+        torch.cuda.synchronize()
+        chunks.append({"wall_ms": (time.perf_counter() - t0) * 1e3, **timer.avg_ms()})
+        del q
+    total_s = time.perf_counter() - t_all
+    pairs = L * (L + 1) // 2
+    sel = sum(min(k, t + 1) for t in range(L))
+    idx_ms = sum(c["indexer"] for c in chunks)
+    mla_ms = sum(c["mla"] for c in chunks)
+    out = {"L": L, "chunk": C, "kv": "fp8_e4m3 + scale", "seconds_total": total_s, "tokens_per_s": L / total_s,
+           "stages_ms_total": {s2: sum(c[s2] for c in chunks) for s2 in ("store", "indexer", "topk", "mla")},
+           "last_chunk_ms": chunks[-1],
+           "indexer_frac_fp8": 2.0 * cfg.h_i * cfg.d_i * pairs / (idx_ms * 1e-3) / 1e12 / PEAK_FP8,
+           "mla_frac_bf16": 2.0 * cfg.h * (576 + 512) * sel / (mla_ms * 1e-3) / 1e12 / PEAK_BF16}
+    if oracle_rows:
+        rows = np.linspace(0, L - 1, oracle_rows).round().astype(np.int64)
+        out["oracle"] = oracle_prefill_rate(inp, cfg, rows, L)
+    del st, inp
+    torch.cuda.empty_cache()
+    return out
+
+
+def sweep_configs(args, dev):
+    """Every config once (C1-C3 prefill, C4 decode, C5 chunked prefill with an FP8
+    latent cache), with oracle rates on row samples: one JSON object."""
+    res = {}
+    for name, orows in (("C1", 1024), ("C2", 128), ("C3", 128)):
+        log(f"[configs] {name}")
+        res[name] = sweep_prefill(name, dev, oracle_rows=orows)
+        log(f"[configs] {name}: {res[name]['ms_per_pass']:.2f} ms")
+    log("[configs] C4")
+    dcfg, dinp, caches, newest, ds, kv_slot = setup_decode_c4(dev)
+    dwall, dst = time_decode(args, dcfg, dinp, caches, newest, ds)
+    gwall, gsame = time_decode_graph(args, dcfg, dinp, caches, newest, ds)
+    db = decode_bytes(dinp, dcfg.k, dcfg.h)
+    res["C4"] = {"batch": dcfg.decode_batch, "us_per_step": dwall * 1e6, "us_per_step_graph": gwall * 1e6,
+                 "graph_matches_eager": gsame, "stages_us": {k2: v * 1e3 for k2, v in dst.items()},
+                 "indexer_frac_hbm": db["indexer_bytes"] / (dst["indexer"] * 1e-3) / 1e9 / PEAK_HBM,
+                 "mla_frac_hbm": db["mla_bytes"] / (dst["mla"] * 1e-3) / 1e9 / PEAK_HBM}
+    res["C4"]["oracle"] = oracle_decode_rate(dinp, dcfg, n_seq=8)
+    del caches, dinp, ds, kv_slot
+    torch.cuda.empty_cache()
+    log("[configs] C5")
+    res["C5"] = sweep_chunked(dev)
+    return res
+
+
 # ---------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -339,6 +494,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--configs", action="store_true",
+                    help="time every config (C1-C5) once with oracle samples instead of the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -346,6 +503,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     dsa.lib()
+    if args.configs:
+        print(json.dumps({"configs": sweep_configs(args, dev)}), flush=True)
+        return
 
     # ---- prefill (headline)
     log("[bench] generating the 32K prefill inputs on the GPU")
