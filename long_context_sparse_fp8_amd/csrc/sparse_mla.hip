@@ -18,12 +18,12 @@
 //     rows x 64 contiguous bytes, each lane keeps one source row for the whole
 //     tile (one slot lookup, then immediate offsets), and both MFMA operand
 //     reads below are bank-conflict free;
-//   * the copies of tile j + 1 and the softmax are spread between the MFMAs of
-//     tile j, so the matrix pipe never waits for address arithmetic or VALU work;
+//   * the copies of tile j + 1 are spread between the MFMAs of tile j, one
+//     every few MFMAs, so their latency is hidden behind the tile's work;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 gathered rows from LDS,
-//     B = the wave's 32 query heads held in VGPRs), in two 32-row halves: the
-//     softmax of half 0 runs under the MFMAs of half 1, that of half 1 under
-//     the first half of O^T += V^T P^T;
+//     B = the wave's 32 query heads held in VGPRs), in two 32-row halves, each
+//     followed by its softmax (a wave's VALU work does not overlap its own
+//     MFMAs here, so spreading the softmax between them measured slower);
 //   * softmax per head (= per lane column) in the exp2 domain against a fixed
 //     reference: the head's maximum over the first 32 rows.  Probabilities of
 //     later rows may exceed 1 by up to 2^64 before the reference must move; that
