@@ -63,6 +63,8 @@ struct TopkShape {
     static constexpr int64_t kMaxRow = C > 0 ? (int64_t)C * 4 * NT : kTopkMaxRow;
     static constexpr int kWords = (int)(kMaxRow / 32);               // bitmap words
     static constexpr int kBinsPer = kBins0 / NT;                     // first-digit bins per thread in the scan
+    static_assert(kCopies0 % 4 == 0, "the scan reads the first histogram's copies four at a time");
+    static_assert(kBins0 % NT == 0, "whole first-digit bins per thread");
 };
 
 template <int NT, int C>
