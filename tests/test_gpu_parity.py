@@ -274,6 +274,36 @@ def test_single_index_gives_value_row():
         np.testing.assert_array_equal(got[t], np.broadcast_to(bits16(kv[sel[t]])[:512], (c.h, 512)))
 
 
+def test_single_index_fp8_cache_every_code():
+    """One selected row of an FP8 cache: the output is that row's 512 value codes
+    times its scale, for every finite E4M3 code (powers-of-two scales keep the
+    product exact in bf16), i.e. the in-kernel expansion of each code is exact."""
+    say("[mla] single index, FP8 cache, all codes")
+    c = CONFIGS["C2"]
+    n, N = 4, 8
+    codes = (np.arange(N * 576) * 37 % 256).astype(np.uint8).reshape(N, 576)   # every code in every row's values
+    codes[codes == 0x7F] = 0x7E                                                 # no NaN codes
+    codes[codes == 0xFF] = 0xFE
+    assert all(len(np.unique(codes[r, :512])) == 254 for r in range(N))
+    scales = np.array([2.0 ** e for e in (-4, 0, 3, -1, 1, 2, -2, 5)], dtype=np.float32)
+    cache = torch.from_numpy(codes).to(DEV)
+    kv_scale = torch.from_numpy(scales).to(DEV)
+    q = synth.bf16_normal((n, c.h, 576), 915).to(DEV)
+    table = torch.arange(N, dtype=torch.int32, device=DEV).reshape(1, N)
+    sel = [5, 0, 2, 7]
+    idx = torch.full((n, 64), -1, dtype=torch.int32)
+    idx[:, 0] = torch.tensor(sel, dtype=torch.int32)
+    out = torch.empty((n, c.h, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((n, c.h), dtype=torch.float32, device=DEV)
+    dsa.sparse_mla_prefill(q, cache, table, torch.zeros(n, dtype=torch.int32, device=DEV), idx.to(DEV),
+                           SM_SCALE, out, lse, kv_scale=kv_scale)
+    torch.cuda.synchronize()
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).float()              # exact decode of each code
+    for t, r in enumerate(sel):
+        want = (dec[r, :512] * float(scales[r]) + 0.0).to(torch.bfloat16)        # -0 accumulates to +0
+        np.testing.assert_array_equal(bits16(out[t].cpu()), np.broadcast_to(bits16(want), (c.h, 512)))
+
+
 def test_empty_selection_and_out_of_range_entries():
     say("[mla] empty / out-of-range entries")
     n, N, h = 4, 100, 16
