@@ -123,6 +123,38 @@ def test_indexer_normal_within_bound(base, L, paged):
     assert max_abs_rel(g[rows][mask], ref[mask]) <= TOL_FP8
 
 
+@pytest.mark.parametrize("n_q", [2, 300])     # the split-key (decode) and query-blocked (prefill) scorers
+def test_indexer_every_code_exact(n_q):
+    """Keys one-hot at 1.0 and unit scales: score[t, s] = ReLU(q[t, 0, s]) exactly,
+    so every finite E4M3 code of q (subnormals, +-0, +-448) goes through the FP8
+    MFMA, the ReLU and the weighting bit-exactly; 128 keys over two shuffled pages."""
+    say(f"[indexer] every code, n_q={n_q}")
+    H, D, N = 64, 128, 128
+    codes = np.arange(256, dtype=np.int64)
+    codes = codes[(codes != 0x7F) & (codes != 0xFF)]                         # 254 finite codes
+    q = np.zeros((n_q, H, D), np.uint8)
+    for t in range(n_q):
+        q[t, 0] = np.roll(codes, -37 * t)[:D] if t % 2 == 0 else np.roll(codes, -37 * t)[D - 2:2 * D - 2]
+    k = np.zeros((N, D), np.uint8)
+    k[np.arange(N), np.arange(N)] = 0x38                                        # E4M3 1.0
+    w = np.zeros((n_q, H), np.float32)
+    w[:, 0] = 1.0
+    page_of = np.array([1, 0])                                                  # logical page -> physical
+    slot = torch.tensor(page_of[np.arange(N) // 64] * 64 + np.arange(N) % 64, dtype=torch.int64, device=DEV)
+    key_cache = torch.zeros((2, 64, D), dtype=torch.uint8, device=DEV)
+    key_scale = torch.zeros((2, 64), dtype=torch.float32, device=DEV)
+    dsa.indexer_cache_store(torch.from_numpy(k).to(DEV), torch.ones(N, device=DEV), slot, key_cache, key_scale)
+    scores = torch.full((n_q, N), -5.0, device=DEV)
+    dsa.indexer_scores(torch.from_numpy(q).to(DEV), torch.ones(n_q, device=DEV), torch.from_numpy(w).to(DEV),
+                       key_cache, key_scale, torch.tensor(page_of, dtype=torch.int32, device=DEV).reshape(1, 2),
+                       torch.zeros(n_q, dtype=torch.int32, device=DEV),
+                       torch.full((n_q,), N - 1, dtype=torch.int32, device=DEV), scores)
+    torch.cuda.synchronize()
+    val = torch.from_numpy(q[:, 0, :].copy()).view(torch.float8_e4m3fn).float().numpy()
+    want = np.maximum(val, 0.0) + 0.0                                           # +0 for every non-positive code
+    np.testing.assert_array_equal(scores.cpu().numpy().view(np.uint32), want.astype(np.float32).view(np.uint32))
+
+
 def test_indexer_shared_weights_and_columns_untouched():
     say("[indexer] shared weights, untouched columns")
     c = CONFIGS["C1"]
