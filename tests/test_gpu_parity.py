@@ -123,20 +123,28 @@ def test_indexer_normal_within_bound(base, L, paged):
     assert max_abs_rel(g[rows][mask], ref[mask]) <= TOL_FP8
 
 
-@pytest.mark.parametrize("n_q", [2, 300])     # the split-key (decode) and query-blocked (prefill) scorers
-def test_indexer_every_code_exact(n_q):
-    """Keys one-hot at 1.0 and unit scales: score[t, s] = ReLU(q[t, 0, s]) exactly,
-    so every finite E4M3 code of q (subnormals, +-0, +-448) goes through the FP8
-    MFMA, the ReLU and the weighting bit-exactly; 128 keys over two shuffled pages."""
-    say(f"[indexer] every code, n_q={n_q}")
+@pytest.mark.parametrize("n_q,side", [(2, "q"), (300, "q"), (2, "k"), (300, "k")])
+def test_indexer_every_code_exact(n_q, side):
+    """side q: keys one-hot at 1.0, so score[t, s] = ReLU(q[t, 0, s]); side k: query
+    head 0 one-hot at dim t % 128, so score[t, s] = ReLU(k[s, t % 128]).  Unit
+    scales and weight: every finite E4M3 code (subnormals, +-0, +-448) on either
+    MFMA operand goes through the scorer, the ReLU and the weighting bit-exactly,
+    in both scorers (n_q = 2: split-key; 300: query-blocked), with 128 keys over
+    two shuffled pages of the fragment-major cache."""
+    say(f"[indexer] every code on {side}, n_q={n_q}")
     H, D, N = 64, 128, 128
     codes = np.arange(256, dtype=np.int64)
     codes = codes[(codes != 0x7F) & (codes != 0xFF)]                         # 254 finite codes
     q = np.zeros((n_q, H, D), np.uint8)
-    for t in range(n_q):
-        q[t, 0] = np.roll(codes, -37 * t)[:D] if t % 2 == 0 else np.roll(codes, -37 * t)[D - 2:2 * D - 2]
     k = np.zeros((N, D), np.uint8)
-    k[np.arange(N), np.arange(N)] = 0x38                                        # E4M3 1.0
+    if side == "q":
+        for t in range(n_q):
+            q[t, 0] = np.roll(codes, -37 * t)[:D] if t % 2 == 0 else np.roll(codes, -37 * t)[D - 2:2 * D - 2]
+        k[np.arange(N), np.arange(N)] = 0x38                                    # E4M3 1.0
+    else:
+        q[np.arange(n_q), 0, np.arange(n_q) % D] = 0x38
+        for s_ in range(N):
+            k[s_] = np.roll(codes, -29 * s_)[:D] if s_ % 2 == 0 else np.roll(codes, -29 * s_)[D - 2:2 * D - 2]
     w = np.zeros((n_q, H), np.float32)
     w[:, 0] = 1.0
     page_of = np.array([1, 0])                                                  # logical page -> physical
@@ -150,7 +158,11 @@ def test_indexer_every_code_exact(n_q):
                        torch.zeros(n_q, dtype=torch.int32, device=DEV),
                        torch.full((n_q,), N - 1, dtype=torch.int32, device=DEV), scores)
     torch.cuda.synchronize()
-    val = torch.from_numpy(q[:, 0, :].copy()).view(torch.float8_e4m3fn).float().numpy()
+    if side == "q":
+        val = torch.from_numpy(q[:, 0, :].copy()).view(torch.float8_e4m3fn).float().numpy()
+    else:
+        kv_ = torch.from_numpy(k.copy()).view(torch.float8_e4m3fn).float().numpy()
+        val = kv_[:, np.arange(n_q) % D].T                                     # [n_q, N]
     want = np.maximum(val, 0.0) + 0.0                                           # +0 for every non-positive code
     np.testing.assert_array_equal(scores.cpu().numpy().view(np.uint32), want.astype(np.float32).view(np.uint32))
 
