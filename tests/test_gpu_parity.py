@@ -280,6 +280,37 @@ def test_sparse_mla_prefill_vs_oracle(base, L, paged, kv_fp8):
     assert el <= 2e-2
 
 
+@pytest.mark.parametrize("h,kv_fp8", [(16, False), (48, True), (64, False), (96, False), (112, True)])
+def test_sparse_mla_head_counts(h, kv_fp8):
+    """Head counts other than 8 and 128 (1 to 4 waves, a partly used last wave;
+    the supported set is 8 and the multiples of 16 up to 128):
+    prefill and decode against the oracle on the same indices."""
+    say(f"[mla heads] h={h} fp8={kv_fp8}")
+    c = _cfg("C1", h=h, k=256)
+    L = 700
+    inp = synth.make_prefill(c, L=L)
+    st = run_prefill(inp, c.k, kv_fp8=kv_fp8)
+    idx = st.idx.cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, L, 37), [L - 1, 255, 256]]))
+    ref_o, ref_l = _mla_ref(inp, idx, rows, kv_fp8)
+    tol = TOL_FP8 if kv_fp8 else TOL_BF16
+    assert max_abs_rel(st.out[rows].float().cpu().numpy(), ref_o) <= tol
+    assert float(np.abs(st.lse[rows].cpu().numpy() - ref_l).max()) <= 2e-2
+    # the same rows through the split decode kernel (3 splits)
+    d = lambda x: x.to(DEV)
+    n = len(rows)
+    need = dsa.sparse_mla_decode_workspace_size(n, h, c.k, 3)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
+    out2 = torch.empty((n, h, 512), dtype=torch.bfloat16, device=DEV)
+    lse2 = torch.empty((n, h), dtype=torch.float32, device=DEV)
+    dsa.sparse_mla_decode(d(inp.q[rows]), st.kv_cache, d(inp.kv_slot_table), torch.zeros(n, dtype=torch.int32,
+                          device=DEV), st.idx[torch.from_numpy(rows).to(DEV)].contiguous(), SM_SCALE, out2, lse2,
+                          kv_scale=st.kv_scale, n_splits=3, ws=ws)
+    torch.cuda.synchronize()
+    assert max_abs_rel(out2.float().cpu().numpy(), ref_o) <= tol
+    assert float(np.abs(lse2.cpu().numpy() - ref_l).max()) <= 2e-2
+
+
 def test_dense_degeneration_k_covers_all():
     """k >= L: every predecessor is selected and the output is dense causal MLA."""
     say("[dense degeneration] C1, k = L")
