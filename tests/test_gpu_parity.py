@@ -167,6 +167,41 @@ def test_indexer_every_code_exact(n_q, side):
     np.testing.assert_array_equal(scores.cpu().numpy().view(np.uint32), want.astype(np.float32).view(np.uint32))
 
 
+@pytest.mark.parametrize("n_q", [4, 300])
+def test_indexer_absent_pages_give_nan(n_q):
+    """A page-table entry of -1, one past n_pages, and a logical page past pt_ld
+    give NaN scores for exactly their 64 tokens; every other score equals the
+    complete table's bit for bit (both scorers)."""
+    say(f"[indexer] absent pages, n_q={n_q}")
+    c = _cfg("C2", paged=True)
+    L = 700
+    inp = synth.make_prefill(c, L=L, materialize_q=False)
+    st = setup_prefill(inp, c.k)
+    rows = np.arange(L - n_q, L)
+    d = lambda x: x.to(DEV)
+    def scores(table):
+        sc = torch.full((n_q, L), -7.0, device=DEV)
+        dsa.indexer_scores(d(inp.iq[rows]), d(inp.iq_scale[rows]), d(inp.w[rows]), st.key_cache, st.key_scale,
+                           table, torch.zeros(n_q, dtype=torch.int32, device=DEV),
+                           d(inp.q_pos[rows]).contiguous(), sc)
+        torch.cuda.synchronize()
+        return sc.cpu().numpy()
+    full = scores(d(inp.page_table).contiguous())
+    bad = inp.page_table.clone()[:, :10].contiguous()          # logical page 10 is past pt_ld
+    bad[0, 3] = -1
+    bad[0, 5] = inp.n_pages + 7
+    got = scores(d(bad))
+    pos = inp.q_pos[rows].numpy()
+    page = np.arange(L) // 64
+    for r in range(n_q):
+        valid = np.arange(L) <= pos[r]
+        gone = valid & np.isin(page, [3, 5, 10])
+        assert np.isnan(got[r, gone]).all(), r
+        keep = valid & ~gone
+        np.testing.assert_array_equal(got[r, keep].view(np.uint32), full[r, keep].view(np.uint32))
+        assert (got[r, ~valid] == -7.0).all()                  # columns past q_pos untouched
+
+
 def test_indexer_shared_weights_and_columns_untouched():
     say("[indexer] shared weights, untouched columns")
     c = CONFIGS["C1"]
