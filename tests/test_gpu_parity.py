@@ -60,6 +60,46 @@ def test_cache_store_bytes(cfg):
     np.testing.assert_array_equal(bits16(st.kv_cache)[kvs], bits16(inp.kv))
 
 
+def test_cache_stores_skip_out_of_range_slots():
+    """Tokens whose slot is negative or past the cache are skipped; every other
+    token lands where its slot says, and nothing else in the caches changes."""
+    say("[cache_store] out-of-range slots")
+    n, n_pages, d_i = 40, 2, 128
+    g = synth.gen(4242)
+    ik = torch.randint(0, 256, (n, d_i), generator=g, dtype=torch.int64).to(torch.uint8)
+    ik[ik == 0x7F] = 0
+    iks = torch.rand(n, generator=g) + 0.5
+    kv = synth.bf16_normal((n, 576), 4243)
+    slot = torch.arange(n, dtype=torch.int64) * 3
+    slot[[1, 7]] = -1
+    slot[[2, 9]] = n_pages * 64 + torch.tensor([0, 5])           # past the indexer cache
+    key_cache = torch.full((n_pages, 64, d_i), 0x11, dtype=torch.uint8, device=DEV)
+    key_scale = torch.full((n_pages, 64), -3.0, device=DEV)
+    dsa.indexer_cache_store(ik.to(DEV), iks.to(DEV), slot.to(DEV), key_cache, key_scale)
+    n_slots = 100
+    kv_slot = slot.clone()
+    kv_slot[kv_slot >= n_slots] = n_slots + 1                     # past the KV cache too
+    kv_cache = torch.full((n_slots, 576), 0x1234, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    dsa.kv_cache_store(kv.to(DEV), kv_slot.to(DEV), kv_cache)
+    torch.cuda.synchronize()
+    rows = key_cache_rows(key_cache, d_i)
+    sc = key_scale.cpu().numpy().reshape(-1)
+    kvc = bits16(kv_cache.cpu())
+    want_rows = np.full((n_pages * 64, d_i), 0x11, np.uint8)
+    want_sc = np.full(n_pages * 64, -3.0, np.float32)
+    want_kv = np.full((n_slots, 576), 0x1234, np.uint16)
+    for i in range(n):
+        sl = int(slot[i])
+        if 0 <= sl < n_pages * 64:
+            want_rows[sl] = u8(ik[i])
+            want_sc[sl] = float(iks[i])
+        if 0 <= int(kv_slot[i]) < n_slots:
+            want_kv[int(kv_slot[i])] = bits16(kv[i])
+    np.testing.assert_array_equal(rows, want_rows)
+    np.testing.assert_array_equal(sc, want_sc)
+    np.testing.assert_array_equal(kvc, want_kv)
+
+
 def test_cache_store_fp8_matches_oracle_quantizer():
     say("[cache_store] fp8 kv")
     n, n_slots = 777, 1000
