@@ -498,7 +498,7 @@ def main():
                     help="time every config (C1-C5) once with oracle samples instead of the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     dev = "cuda:0"
     torch.cuda.set_device(0)
