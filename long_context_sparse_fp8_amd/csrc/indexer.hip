@@ -203,12 +203,12 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
             }
             const float ksc = sbuf[buf][lane];
             const int64_t key = p * kPage + lane;
+            // Every query of the wave is scored, active or not (an inactive one's
+            // scores are not stored): with no branch between them the compiler
+            // can put one query's MFMAs under the other's epilogue.
             float sc[QPW];
 #pragma unroll
-            for (int qq = 0; qq < QPW; ++qq) {
-                const int r = wave * QPW + qq;
-                sc[qq] = (active >> r) & 1u ? page_scores<H_I, D_I>(q[qq], b) : 0.0f;
-            }
+            for (int qq = 0; qq < QPW; ++qq) sc[qq] = page_scores<H_I, D_I>(q[qq], b);
             // the next page goes to LDS before the score stores: loads and stores
             // share one counter, so a store issued first would be waited for too
             if (p + 1 < n_pg) commit(buf ^ 1);
