@@ -83,6 +83,8 @@ def test_topk_validation(L):
     # few long rows split over workgroups: survivors (score + index) per part
     assert L.dsa_topk_workspace_size(64, 131072, 2048) == 64 * 4 * 2048 * 8 + 256
     assert L.dsa_topk_workspace_size(16, 131072, 2048) == 16 * 8 * 2048 * 8 + 256
+    assert L.dsa_topk_workspace_size(128, 131072, 2048) == 128 * 4 * 2048 * 8 + 256   # parts of <= 32K
+    assert L.dsa_topk_workspace_size(128, 32768, 2048) == 128 * 2 * 2048 * 8 + 256
     assert L.dsa_topk_workspace_size(300, 131072, 2048) == 0
 
 
