@@ -35,6 +35,9 @@
  *    gathered address: an entry that points outside its table or cache is
  *    skipped as documented per function, never dereferenced.
  *  - Pointers must be 16-byte aligned (DSA_ERR_MISALIGNED otherwise).
+ *  - A zero count (n = 0, n_q = 0) is valid: the shape, dtype and support
+ *    checks still apply, the data pointers may be NULL, and nothing is
+ *    enqueued.
  *
  * FP8 is OCP E4M3 ("e4m3fn": bias 7, max 448, no infinities, S.1111.111 =
  * NaN), the "fp8_e4m3" KV-cache dtype of the deployment article, section 3.

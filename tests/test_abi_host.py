@@ -120,3 +120,25 @@ def test_cache_store_validation(L):
     assert L.dsa_kv_cache_store(A, A, 10, 2, A, A, 100, None) == 3
     assert L.dsa_kv_cache_store(A, A, 10, 1, A, None, 100, None) == 1
     assert L.dsa_kv_cache_store(A, MIS, 10, 0, A, None, 100, None) == 4
+
+
+def test_zero_counts_enqueue_nothing(L):
+    """n = 0 / n_q = 0: OK with NULL data pointers (no device needed), while the
+    shape and support checks still apply."""
+    f = ctypes.c_float(1 / 24)
+    assert L.dsa_indexer_cache_store(None, None, None, 0, 128, None, None, 4, None) == 0
+    assert L.dsa_indexer_cache_store(None, None, None, 0, 96, None, None, 4, None) == 3
+    assert L.dsa_kv_cache_store(None, None, 0, 0, None, None, 10, None) == 0
+    assert L.dsa_kv_cache_store(None, None, 0, 1, None, None, 10, None) == 0
+    assert L.dsa_kv_cache_store(None, None, 0, 7, None, None, 10, None) == 3
+    assert L.dsa_indexer_scores(None, None, None, 0, None, None, 10, None, 4, None, None, 0, 64, 128,
+                                None, 100, None) == 0
+    assert L.dsa_topk(None, 100, None, 0, 16, None, None, 0, None) == 0
+    assert L.dsa_topk(None, 100, None, 0, 0, None, None, 0, None) == 3
+    for fn in (L.dsa_sparse_mla_prefill,):
+        assert fn(None, None, None, 0, 100, None, 100, None, None, 0, 128, 2048, f, None, None, None) == 0
+        assert fn(None, None, None, 0, 100, None, 100, None, None, 0, 24, 2048, f, None, None, None) == 3
+    assert L.dsa_sparse_mla_decode(None, None, None, 0, 100, None, 100, None, None, 0, 128, 2048, f, None, None,
+                                   0, None, 0, None) == 0
+    assert L.dsa_sparse_mla_decode(None, None, None, 0, 100, None, 100, None, None, 0, 128, 2048, f, None, None,
+                                   40, None, 0, None) == 3
