@@ -11,7 +11,7 @@
 // overlap the other's work), else 1024.  Every score is touched by only three
 // cheap sweeps:
 //   1. an 11-bit histogram of the top key bits (sign, exponent, two mantissa
-//      bits) in LDS, eight lane-interleaved copies; a block scan of the 2048
+//      bits) in LDS, NT / 128 lane-interleaved copies; a block scan of the 2048
 //      bins from the top finds the bin holding the k-th largest key;
 //   2. the keys of that bin (a few percent of the row) are collected into an
 //      LDS candidate list, and the radix select finishes on the list alone
