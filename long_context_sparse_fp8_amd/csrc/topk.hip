@@ -490,9 +490,11 @@ static void launch_rows(dim3 grid, int64_t len, bool vec, const float *scores, i
 #define DSA_TOPK_GO(NT, C, V)                                                                                    \
     hipLaunchKernelGGL((topk_kernel<NT, C, V, MODE>), grid, dim3(NT), 0, stream, scores, ld, q_pos, k, idx, parts,    \
                        ws_score, ws_idx)
-    if constexpr (MODE == kWholeRow) {
-        // many rows: two workgroups of 512 per CU while a row fits their registers
-        if (len <= 16 * 2048) {
+    if constexpr (MODE != kMerge) {
+        // more rows (or parts) than a 256-CU device has CUs: two workgroups of 512
+        // per CU while a row fits their registers (128 decode rows in 4 parts:
+        // 58 -> 51 us); with fewer, one workgroup of 1024 per row
+        if (len <= 16 * 2048 && (int64_t)grid.x * grid.y > 256) {
             if (vec) {
                 if (len <= 8 * 2048) DSA_TOPK_GO(512, 8, true);
                 else DSA_TOPK_GO(512, 16, true);
