@@ -264,7 +264,7 @@ def test_indexer_shared_weights_and_columns_untouched():
 
 # ------------------------------------------------------------------ top-k
 @pytest.mark.parametrize("case", ["normal", "ties", "zeros", "short_rows", "wide", "odd_ld", "mid", "mid_ties",
-                                  "split_ties", "split_mixed", "split_long"])
+                                  "split_ties", "split_mixed", "split_long", "max_row"])
 def test_topk_bitexact_from_identical_scores(case):
     say(f"[topk] {case}")
     rng = np.random.default_rng(sum(map(ord, case)))
@@ -281,6 +281,8 @@ def test_topk_bitexact_from_identical_scores(case):
         n_q, ld, k = 64, 40000, 333 if case == "split_ties" else 2048
     if case == "split_long":        # 128 rows whose two parts would exceed 32K: four parts instead
         n_q, ld, k = 128, 70000, 2048
+    if case == "max_row":           # the longest row the ABI accepts (DSA_MAX_TOPK_ROW)
+        n_q, ld, k = 8, 262144, 2048
     s = rng.standard_normal((n_q, ld)).astype(np.float32)
     if case in ("ties", "split_ties"):
         s = np.round(s * 2) / 2
