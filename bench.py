@@ -573,6 +573,7 @@ def main():
         }
         for v in dk.values():
             v["frac"] = v["achieved"] / v["peak"]
+        dk["indexer"]["traffic"] = recorded_traffic("indexer_decode")
         result["decode"] = {"workload": "decode: 64 sequences x 1 query, context ~ U[32768, 131072] "
                                         f"(mean {float(dinp.lens.float().mean()):.0f}), k=2048, bf16 latent cache",
                             "us_per_step": dwall * 1e6, "tokens_per_s": dcfg.decode_batch / dwall,
