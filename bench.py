@@ -245,7 +245,7 @@ def run_decode_step(cfg, inp, caches, newest, ds, timer=None):
                        inp.q_pos, ds.scores)
     if e: e.record()
     e = t("topk")
-    dsa.topk(ds.scores, inp.q_pos, cfg.k, ds.idx)
+    dsa.topk(ds.scores, inp.q_pos, cfg.k, ds.idx, ws=ds.topk_ws)
     if e: e.record()
     e = t("mla")
     dsa.sparse_mla_decode(inp.q, caches.kv_cache, inp.kv_slot_table, inp.q_seq, ds.idx, SM_SCALE, ds.out, ds.lse,

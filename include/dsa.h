@@ -204,7 +204,7 @@ dsa_status dsa_topk(const float *scores, int64_t scores_ld, const int32_t *q_pos
  * A query with no valid index gets out = 0 and lse = -inf.
  * bf16 MFMA with fp32 accumulation and an online softmax; FP8 rows are
  * expanded to bf16 exactly and their per-row scale applied in fp32.
- * Supported: h a multiple of 16 in [16, 128], or h = 8; 1 <= k <= 2048. */
+ * Supported: h a multiple of 8 in [8, 128]; 1 <= k <= 2048. */
 dsa_status dsa_sparse_mla_prefill(const uint16_t *q, const void *kv_cache, const float *kv_scale,
                                   dsa_kv_dtype dt, int64_t n_slots,
                                   const int32_t *kv_slot_table, int64_t kv_pt_ld,

@@ -152,8 +152,8 @@ dsa_status check_mla(const char *fn, const uint16_t *q, const void *kv_cache, co
                      const int32_t *idx, int32_t n_q, int32_t h, int32_t k, float sm_scale, uint16_t *out,
                      float *lse) {
     REQUIRE(n_q >= 0, DSA_ERR_BAD_SHAPE, "%s: n_q = %d < 0", fn, n_q);
-    REQUIRE(h == 8 || (h >= 16 && h <= 128 && h % 16 == 0), DSA_ERR_UNSUPPORTED,
-            "%s: h = %d (need 8 or a multiple of 16 in [16, 128])", fn, h);
+    REQUIRE(h >= 8 && h <= 128 && h % 8 == 0, DSA_ERR_UNSUPPORTED, "%s: h = %d (need a multiple of 8 in [8, 128])",
+            fn, h);
     REQUIRE(k >= 1 && k <= DSA_MAX_TOPK, DSA_ERR_UNSUPPORTED, "%s: k = %d not in [1, %d]", fn, k, DSA_MAX_TOPK);
     REQUIRE(dt == DSA_KV_BF16 || dt == DSA_KV_FP8_E4M3, DSA_ERR_UNSUPPORTED, "%s: bad kv dtype %d", fn, (int)dt);
     REQUIRE(n_slots >= 1 && kv_pt_ld >= 1, DSA_ERR_BAD_SHAPE, "%s: n_slots / kv_pt_ld must be >= 1", fn);

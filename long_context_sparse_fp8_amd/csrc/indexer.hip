@@ -14,6 +14,8 @@
 // and most of the head sum stay in the lane; one half-wave swap finishes the
 // head sum and leaves key l of the 64-key page in lane l for a coalesced
 // store.
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -411,8 +413,11 @@ template <int H_I, int D_I>
 static hipError_t launch_indexer_t(const IndexerArgs &a, hipStream_t stream) {
     if (a.n_q <= kIndexerDecodeMaxQ) {
         // few queries: split each query's key range over workgroups
+        // Splits cover every logical page a score row can reach: those of the page
+        // table and those past it (up to the row length), which get NaN scores.
         const int pps = 4 * kWavePages;            // 64: one page-table entry per lane
-        const int64_t splits = (a.pt_ld + pps - 1) / pps;
+        const int64_t row_pages = (a.scores_ld + kPage - 1) / kPage;
+        const int64_t splits = (std::max(a.pt_ld, row_pages) + pps - 1) / pps;
         dim3 grid((unsigned)a.n_q, (unsigned)(splits > 0 ? splits : 1));
         hipLaunchKernelGGL((indexer_decode_kernel<H_I, D_I>), grid, dim3(256), 0, stream, a.q_fp8, a.q_scale, a.w,
                            a.w_ld, a.key_cache, a.key_scale, a.n_pages, a.page_table, a.pt_ld, a.q_seq, a.q_pos,

@@ -175,10 +175,18 @@ __device__ __noinline__ void pick_digit(TopkSmem<NT, C> &sm, int nb, uint32_t re
 
 enum TopkMode { kWholeRow = 0, kPart = 1, kMerge = 2 };
 
-// Parts of a row of n scores when splitting into at most `parts` (each part
-// holds at least 2k scores).
+// Parts of a row of n scores when splitting into at most `parts`.  Every part
+// must hold more than k scores, so that it runs the selection and leaves its k
+// survivors in the workspace (a part of at most k scores would take the
+// keep-everything exit instead).  Parts are whole 4-score groups: with
+// q = ceil(n / 4) groups over P parts, the shortest part holds at least
+// 4 floor(q / P) - 3 scores (the last one may end short), which exceeds k
+// once floor(q / P) >= ceil((k + 4) / 4).  For k >= 4 the first bound (at
+// least 2k scores per part on average) already implies it; it matters for
+// k < 4, e.g. k = 1 on a row of 8 scores.
 __device__ __forceinline__ int topk_row_parts(int n, int k, int parts) {
-    return max(1, min(parts, n / (2 * k)));
+    const int groups_per_part = (k + 7) / 4;   // ceil((k + 4) / 4)
+    return max(1, min(min(parts, n / (2 * k)), ((n + 3) / 4) / groups_per_part));
 }
 
 // C > 0: rows of at most C chunks, keys held in registers.  C == 0: chunks are

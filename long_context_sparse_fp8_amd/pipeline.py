@@ -66,26 +66,30 @@ class DecodeState:
     idx: torch.Tensor              # [B, k] int32
     out: torch.Tensor              # [B, H, 512] bf16
     lse: torch.Tensor              # [B, H] f32
-    ws: torch.Tensor               # decode workspace (uint8)
+    ws: torch.Tensor               # sparse MLA decode workspace (uint8)
     n_splits: int
+    topk_ws: Optional[torch.Tensor] = None   # top-k workspace (uint8), None when rows are not split
 
 
 def alloc_decode(batch, ld, k, h, n_splits=0, device="cuda"):
     """Buffers of one decode step over contexts of up to `ld` tokens.  The score
     rows are padded to a multiple of 64 columns so every row is 256-byte aligned
-    (the top-k then reads them with 16-byte vector loads)."""
+    (the top-k then reads them with 16-byte vector loads).  Both workspaces are
+    allocated here, so a step allocates nothing."""
     need = B.sparse_mla_decode_workspace_size(batch, h, k, n_splits)
     ld = (ld + 63) // 64 * 64
+    tk = B.topk_workspace_size(batch, ld, k)
     return DecodeState(scores=torch.empty((batch, ld), dtype=torch.float32, device=device),
                        idx=torch.empty((batch, k), dtype=torch.int32, device=device),
                        out=torch.empty((batch, h, B.DV), dtype=torch.bfloat16, device=device),
                        lse=torch.empty((batch, h), dtype=torch.float32, device=device),
-                       ws=torch.empty(max(need, 1), dtype=torch.uint8, device=device), n_splits=n_splits)
+                       ws=torch.empty(max(need, 1), dtype=torch.uint8, device=device), n_splits=n_splits,
+                       topk_ws=torch.empty(tk, dtype=torch.uint8, device=device) if tk else None)
 
 
 def decode_step(ds: DecodeState, caches: PrefillState, iq, iq_scale, w, page_table, kv_slot_table, q_seq, q_pos, q,
                 k, sm_scale):
     B.indexer_scores(iq, iq_scale, w, caches.key_cache, caches.key_scale, page_table, q_seq, q_pos, ds.scores)
-    B.topk(ds.scores, q_pos, k, ds.idx)
+    B.topk(ds.scores, q_pos, k, ds.idx, ws=ds.topk_ws)
     B.sparse_mla_decode(q, caches.kv_cache, kv_slot_table, q_seq, ds.idx, sm_scale, ds.out, ds.lse,
                         kv_scale=caches.kv_scale, n_splits=ds.n_splits, ws=ds.ws)

@@ -93,7 +93,8 @@ def test_mla_validation(L):
     args = lambda **kw: [kw.get("q", A), A, kw.get("kvs", A), kw.get("dt", 0), kw.get("n_slots", 100), A,
                          kw.get("ld", 100), A, A, kw.get("n_q", 4), kw.get("h", 128), kw.get("k", 2048),
                          kw.get("sm", f), A, kw.get("lse", None)]
-    assert L.dsa_sparse_mla_prefill(*args(h=24), None) == 3
+    assert L.dsa_sparse_mla_prefill(*args(h=20), None) == 3   # head counts are multiples of 8
+    assert L.dsa_sparse_mla_prefill(*args(h=0), None) == 3
     assert L.dsa_sparse_mla_prefill(*args(h=144), None) == 3
     assert L.dsa_sparse_mla_prefill(*args(k=0), None) == 3
     assert L.dsa_sparse_mla_prefill(*args(k=4096), None) == 3
@@ -137,7 +138,8 @@ def test_zero_counts_enqueue_nothing(L):
     assert L.dsa_topk(None, 100, None, 0, 0, None, None, 0, None) == 3
     for fn in (L.dsa_sparse_mla_prefill,):
         assert fn(None, None, None, 0, 100, None, 100, None, None, 0, 128, 2048, f, None, None, None) == 0
-        assert fn(None, None, None, 0, 100, None, 100, None, None, 0, 24, 2048, f, None, None, None) == 3
+        assert fn(None, None, None, 0, 100, None, 100, None, None, 0, 24, 2048, f, None, None, None) == 0
+        assert fn(None, None, None, 0, 100, None, 100, None, None, 0, 12, 2048, f, None, None, None) == 3
     assert L.dsa_sparse_mla_decode(None, None, None, 0, 100, None, 100, None, None, 0, 128, 2048, f, None, None,
                                    0, None, 0, None) == 0
     assert L.dsa_sparse_mla_decode(None, None, None, 0, 100, None, 100, None, None, 0, 128, 2048, f, None, None,
