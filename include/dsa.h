@@ -212,16 +212,21 @@ dsa_status dsa_sparse_mla_prefill(const uint16_t *q, const void *kv_cache, const
                                   int32_t k, float sm_scale, uint16_t *out, float *lse, void *stream);
 
 /* Bytes of workspace dsa_sparse_mla_decode needs (n_splits = 0: the value
- * the library would pick automatically for these sizes). */
+ * the library would pick automatically for these sizes); 0 when the index lists
+ * are not split. */
 size_t dsa_sparse_mla_decode_workspace_size(int32_t n_q, int32_t h, int32_t k, int32_t n_splits);
 
-/* Decode form of dsa_sparse_mla_prefill for few queries (one per
- * sequence): same arguments and result, but each query's index list is cut
- * into n_splits chunks processed in parallel, each producing a partial
- * output and log-sum-exp in `ws`, merged afterwards with LSE weights.
- * n_splits = 0 picks a split count from n_q and k; otherwise
- * 1 <= n_splits <= 32.  ws_bytes must be at least
- * dsa_sparse_mla_decode_workspace_size(n_q, h, k, n_splits). */
+/* Decode form of dsa_sparse_mla_prefill for few queries (one or a few per
+ * sequence): same arguments and result.
+ *   n_splits = 1: one workgroup per (query, group of 32 heads) attends over the
+ *     query's whole selection; no workspace (ws may be NULL).
+ *   n_splits > 1 (at most 32): each query's index list is cut into n_splits
+ *     chunks processed in parallel, each producing a partial output and
+ *     log-sum-exp in `ws`, merged afterwards with LSE weights.
+ *   n_splits = 0 picks: 1 when n_q * ceil(h / 32) >= 128, else a split count
+ *     that gives about one workgroup per compute unit.
+ * ws_bytes must be at least dsa_sparse_mla_decode_workspace_size(n_q, h, k,
+ * n_splits) (DSA_ERR_WORKSPACE_TOO_SMALL otherwise). */
 dsa_status dsa_sparse_mla_decode(const uint16_t *q, const void *kv_cache, const float *kv_scale,
                                  dsa_kv_dtype dt, int64_t n_slots,
                                  const int32_t *kv_slot_table, int64_t kv_pt_ld,

@@ -188,7 +188,7 @@ DSA_EXPORT dsa_status dsa_sparse_mla_prefill(const uint16_t *q, const void *kv_c
 
 DSA_EXPORT size_t dsa_sparse_mla_decode_workspace_size(int32_t n_q, int32_t h, int32_t k, int32_t n_splits) {
     if (n_q <= 0 || h <= 0 || k <= 0) return 0;
-    if (n_splits <= 0) n_splits = dsa::mla_decode_auto_splits(n_q, k);
+    if (n_splits <= 0) n_splits = dsa::mla_decode_auto_splits(n_q, h, k);
     return dsa::mla_decode_ws_bytes(n_q, h, n_splits);
 }
 
@@ -203,11 +203,11 @@ DSA_EXPORT dsa_status dsa_sparse_mla_decode(const uint16_t *q, const void *kv_ca
     REQUIRE(n_splits >= 0 && n_splits <= 32, DSA_ERR_UNSUPPORTED, "dsa_sparse_mla_decode: n_splits = %d not in [0, 32]",
             n_splits);
     if (n_q == 0) return DSA_OK;
-    if (n_splits == 0) n_splits = dsa::mla_decode_auto_splits(n_q, k);
+    if (n_splits == 0) n_splits = dsa::mla_decode_auto_splits(n_q, h, k);
     const size_t need = dsa::mla_decode_ws_bytes(n_q, h, n_splits);
     REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL,
             "dsa_sparse_mla_decode: ws_bytes = %zu < %zu needed", ws_bytes, need);
-    REQUIRE_PTR(ws);
+    if (need > 0) REQUIRE_PTR(ws);
     dsa::MlaArgs a{q, kv_cache, kv_scale, dt == DSA_KV_FP8_E4M3, n_slots, kv_slot_table, kv_pt_ld, q_seq, idx,
                    n_q, h, k, sm_scale, out, lse};
     hipError_t e = dsa::launch_mla_decode(a, n_splits, ws, (hipStream_t)stream);

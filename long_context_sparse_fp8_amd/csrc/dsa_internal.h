@@ -72,7 +72,7 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, in
 size_t topk_ws_bytes(int32_t n_q, int64_t ld, int32_t k);
 hipError_t launch_mla_prefill(const MlaArgs &a, hipStream_t stream);
 hipError_t launch_mla_decode(const MlaArgs &a, int n_splits, void *ws, hipStream_t stream);
-int mla_decode_auto_splits(int32_t n_q, int32_t k);
+int mla_decode_auto_splits(int32_t n_q, int32_t h, int32_t k);
 size_t mla_decode_ws_bytes(int32_t n_q, int32_t h, int32_t n_splits);
 
 }  // namespace dsa

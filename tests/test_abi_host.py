@@ -104,13 +104,16 @@ def test_mla_validation(L):
     assert L.dsa_sparse_mla_prefill(*args(q=None), None) == 1
     assert L.dsa_sparse_mla_prefill(*args(dt=1, kvs=None), None) == 1
     assert L.dsa_sparse_mla_prefill(*args(lse=MIS), None) == 4
-    need = L.dsa_sparse_mla_decode_workspace_size(64, 128, 2048, 0)
-    assert need > 0
-    assert L.dsa_sparse_mla_decode(*args(n_q=64), 0, A, need - 1, None) == 5
+    # one workgroup per (query, 32 heads) needs no workspace: the automatic choice
+    # when queries x head groups fill half the device
+    assert L.dsa_sparse_mla_decode_workspace_size(64, 128, 2048, 0) == 0
+    assert L.dsa_sparse_mla_decode_workspace_size(64, 128, 2048, 1) == 0
+    assert L.dsa_sparse_mla_decode_workspace_size(8, 128, 2048, 0) > 0      # few queries: split index lists
+    need = L.dsa_sparse_mla_decode_workspace_size(64, 128, 2048, 4)
+    assert need == 64 * 4 * 128 * 512 * 4 + ((64 * 4 * 128 * 4 + 255) // 256) * 256 + 256
+    assert L.dsa_sparse_mla_decode(*args(n_q=64), 4, A, need - 1, None) == 5
     assert L.dsa_sparse_mla_decode(*args(n_q=64), 33, A, need, None) == 3
-    assert L.dsa_sparse_mla_decode(*args(n_q=64), 0, None, need, None) == 1
-    assert L.dsa_sparse_mla_decode_workspace_size(64, 128, 2048, 4) == 64 * 4 * 128 * 512 * 4 + \
-        ((64 * 4 * 128 * 4 + 255) // 256) * 256 + 256
+    assert L.dsa_sparse_mla_decode(*args(n_q=64), 4, None, need, None) == 1
 
 
 def test_cache_store_validation(L):

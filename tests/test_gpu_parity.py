@@ -428,19 +428,21 @@ def test_sparse_mla_head_counts(h, kv_fp8):
     tol = TOL_FP8 if kv_fp8 else TOL_BF16
     assert max_abs_rel(st.out[rows].float().cpu().numpy(), ref_o) <= tol
     assert float(np.abs(st.lse[rows].cpu().numpy() - ref_l).max()) <= 2e-2
-    # the same rows through the split decode kernel (3 splits)
+    # the same rows through both decode forms: 3 splits, and one workgroup per
+    # (query, 32 heads) with a partly used last head group
     d = lambda x: x.to(DEV)
     n = len(rows)
-    need = dsa.sparse_mla_decode_workspace_size(n, h, c.k, 3)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
-    out2 = torch.empty((n, h, 512), dtype=torch.bfloat16, device=DEV)
-    lse2 = torch.empty((n, h), dtype=torch.float32, device=DEV)
-    dsa.sparse_mla_decode(d(inp.q[rows]), st.kv_cache, d(inp.kv_slot_table), torch.zeros(n, dtype=torch.int32,
-                          device=DEV), st.idx[torch.from_numpy(rows).to(DEV)].contiguous(), SM_SCALE, out2, lse2,
-                          kv_scale=st.kv_scale, n_splits=3, ws=ws)
-    torch.cuda.synchronize()
-    assert max_abs_rel(out2.float().cpu().numpy(), ref_o) <= tol
-    assert float(np.abs(lse2.cpu().numpy() - ref_l).max()) <= 2e-2
+    for n_splits in (3, 1):
+        need = dsa.sparse_mla_decode_workspace_size(n, h, c.k, n_splits)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
+        out2 = torch.empty((n, h, 512), dtype=torch.bfloat16, device=DEV)
+        lse2 = torch.empty((n, h), dtype=torch.float32, device=DEV)
+        dsa.sparse_mla_decode(d(inp.q[rows]), st.kv_cache, d(inp.kv_slot_table), torch.zeros(n, dtype=torch.int32,
+                              device=DEV), st.idx[torch.from_numpy(rows).to(DEV)].contiguous(), SM_SCALE, out2, lse2,
+                              kv_scale=st.kv_scale, n_splits=n_splits, ws=ws)
+        torch.cuda.synchronize()
+        assert max_abs_rel(out2.float().cpu().numpy(), ref_o) <= tol, n_splits
+        assert float(np.abs(lse2.cpu().numpy() - ref_l).max()) <= 2e-2, n_splits
 
 
 def _restart_inputs(case, n=4, h=128, k=512, seed=0):
@@ -682,9 +684,14 @@ def test_chunked_equals_monolithic():
 @pytest.mark.parametrize("batch,lo,hi,n_splits,kv_fp8,m", [(8, 2000, 9000, 0, False, 1), (5, 100, 3000, 3, False, 1),
                                                            (3, 2049, 2049, 1, False, 1), (6, 1500, 7000, 0, True, 1),
                                                            (4, 2049, 4100, 2, True, 1), (5, 1900, 6000, 0, False, 3),
-                                                           (4, 2050, 2052, 2, True, 2)])
+                                                           (4, 2050, 2052, 2, True, 2), (8, 100, 3000, 1, False, 1),
+                                                           (6, 1500, 7000, 1, True, 1), (5, 1900, 6000, 1, False, 3),
+                                                           (7, 2041, 2100, 1, True, 2)])
 def test_decode_vs_oracle(batch, lo, hi, n_splits, kv_fp8, m):
-    """m query tokens per sequence (m > 1: the multi-token-prediction shape)."""
+    """m query tokens per sequence (m > 1: the multi-token-prediction shape).
+    n_splits = 1: one workgroup per (query, 32 heads) over the whole selection
+    (contexts below k leave waves with few or no rows); 2, 3: split index lists
+    merged by a second launch; 0: the automatic choice."""
     say(f"[decode] B={batch} ctx=[{lo},{hi}] splits={n_splits} fp8={kv_fp8} queries/seq={m}")
     c = CONFIGS["C4"]
     inp = synth.make_decode(c, batch=batch, ctx_lo=lo, ctx_hi=hi, queries_per_seq=m)
