@@ -180,6 +180,19 @@ size_t dsa_topk_workspace_size(int32_t n_q, int64_t max_len, int32_t k);
 dsa_status dsa_topk(const float *scores, int64_t scores_ld, const int32_t *q_pos, int32_t n_q, int32_t k,
                     int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 
+/* dsa_topk for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same selection
+ * and result, with the split rows' survivors in a static device array of the
+ * library (8 MiB + 256 bytes per device, held until the process ends) instead
+ * of a caller workspace.  Nothing is allocated or freed; the array's address
+ * is looked up once per device, on the first call with that device current
+ * (the stream must belong to the current device).  Calls that overlap on one
+ * device share the array and race: serialise them (one stream, or events).
+ * Sizes whose split would exceed the array return DSA_ERR_WORKSPACE_TOO_SMALL
+ * (none does for k <= 2048); otherwise arguments and errors as dsa_topk. */
+dsa_status dsa_topk_static(const float *scores, int64_t scores_ld, const int32_t *q_pos, int32_t n_q, int32_t k,
+                           int32_t *idx, void *stream);
+
 /* ------------------------------------------------------------------------
  * Stage 3: sparse MLA over the selected latent rows
  * ------------------------------------------------------------------------ */

@@ -55,6 +55,8 @@ def lib():
     L.dsa_topk_workspace_size.argtypes = [i32, i64, i32]
     L.dsa_topk.restype = ctypes.c_int
     L.dsa_topk.argtypes = [P, i64, P, i32, i32, P, P, sz, P]
+    L.dsa_topk_static.restype = ctypes.c_int
+    L.dsa_topk_static.argtypes = [P, i64, P, i32, i32, P, P]
     L.dsa_sparse_mla_prefill.restype = ctypes.c_int
     L.dsa_sparse_mla_prefill.argtypes = [P, P, P, ctypes.c_int, i64, P, i64, P, P, i32, i32, i32, f32, P, P, P]
     L.dsa_sparse_mla_decode_workspace_size.restype = sz
@@ -155,6 +157,13 @@ def topk(scores, q_pos, k, idx, ws=None, stream=None):
     _check(lib().dsa_topk(_ptr(scores, torch.float32, "scores"), ld, _ptr(q_pos, torch.int32, "q_pos"), n_q, k,
                           _ptr(idx, torch.int32, "idx"), _ptr(ws, None, "ws") if need else None,
                           need, _stream(stream)))
+
+
+def topk_static(scores, q_pos, k, idx, stream=None):
+    """topk with the library's static workspace (allocates nothing, no workspace argument)."""
+    n_q, ld = scores.shape
+    _check(lib().dsa_topk_static(_ptr(scores, torch.float32, "scores"), ld, _ptr(q_pos, torch.int32, "q_pos"), n_q,
+                                 k, _ptr(idx, torch.int32, "idx"), _stream(stream)))
 
 
 # ---------------------------------------------------------------- stage 3

@@ -146,6 +146,33 @@ DSA_EXPORT dsa_status dsa_topk(const float *scores, int64_t scores_ld, const int
     return DSA_OK;
 }
 
+DSA_EXPORT dsa_status dsa_topk_static(const float *scores, int64_t scores_ld, const int32_t *q_pos, int32_t n_q,
+                                      int32_t k, int32_t *idx, void *stream) {
+    REQUIRE(n_q >= 0, DSA_ERR_BAD_SHAPE, "dsa_topk_static: n_q = %d < 0", n_q);
+    REQUIRE(k >= 1 && k <= DSA_MAX_TOPK, DSA_ERR_UNSUPPORTED, "dsa_topk_static: k = %d not in [1, %d]", k,
+            DSA_MAX_TOPK);
+    REQUIRE(scores_ld >= 1, DSA_ERR_BAD_SHAPE, "dsa_topk_static: scores_ld = %lld < 1", (long long)scores_ld);
+    REQUIRE(scores_ld <= DSA_MAX_TOPK_ROW, DSA_ERR_UNSUPPORTED, "dsa_topk_static: scores_ld = %lld > %d",
+            (long long)scores_ld, DSA_MAX_TOPK_ROW);
+    if (n_q == 0) return DSA_OK;
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(q_pos);
+    REQUIRE_PTR(idx);
+    const size_t need = dsa::topk_ws_bytes(n_q, scores_ld, k);
+    void *ws = nullptr;
+    size_t cap = 0;
+    if (need > 0) {
+        hipError_t e = dsa::topk_static_workspace(&ws, &cap);
+        if (e != hipSuccess) return hip_fail(e, "dsa_topk_static: static workspace lookup");
+        REQUIRE(need <= cap, DSA_ERR_WORKSPACE_TOO_SMALL,
+                "dsa_topk_static: the split rows need %zu bytes, more than the static workspace's %zu", need, cap);
+    }
+    hipError_t e = dsa::launch_topk(scores, scores_ld, q_pos, n_q, k, idx, ws, need > 0 ? cap : 0,
+                                    (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "dsa_topk_static launch");
+    return DSA_OK;
+}
+
 namespace {
 dsa_status check_mla(const char *fn, const uint16_t *q, const void *kv_cache, const float *kv_scale, dsa_kv_dtype dt,
                      int64_t n_slots, const int32_t *kv_slot_table, int64_t kv_pt_ld, const int32_t *q_seq,

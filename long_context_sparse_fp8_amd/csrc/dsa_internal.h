@@ -70,6 +70,8 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, in
 // Workspace that lets dsa_topk split few long rows over several workgroups
 // (0 when it does not split at these sizes).
 size_t topk_ws_bytes(int32_t n_q, int64_t ld, int32_t k);
+// The current device's static top-k workspace (looked up once per device) and its size.
+hipError_t topk_static_workspace(void **ptr, size_t *bytes);
 hipError_t launch_mla_prefill(const MlaArgs &a, hipStream_t stream);
 hipError_t launch_mla_decode(const MlaArgs &a, int n_splits, void *ws, hipStream_t stream);
 int mla_decode_auto_splits(int32_t n_q, int32_t h, int32_t k);

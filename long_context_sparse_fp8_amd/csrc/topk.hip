@@ -40,6 +40,7 @@
 // ties between survivors still fall to the lower original index, so the result
 // is the same as the one-workgroup selection.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "dsa_device.h"
@@ -522,6 +523,41 @@ static void launch_rows(dim3 grid, int64_t len, bool vec, const float *scores, i
         else DSA_TOPK_GO(1024, 0, false);
     }
 #undef DSA_TOPK_GO
+}
+
+// ---------------------------------------------------------------- static workspace
+// The split rows' survivors of dsa_topk_static live in this file-scope device
+// array instead of a caller workspace, for callers that cannot allocate (HIP
+// graph capture, serving loops).  Every split made above fits: at most 512
+// parts (rows x parts) of k <= 2048 survivors of 8 bytes, plus the 256-byte
+// alignment slack, 8 MiB + 256 bytes per device, held until the process ends.
+// Every call on a device shares that device's copy; nothing in it must start
+// at zero (each part writes all of its survivors before the merge reads them).
+constexpr size_t kTopkStaticBytes = (size_t)512 * kTopkMaxK * (sizeof(float) + sizeof(int32_t)) + 256;
+static __device__ __align__(256) uint8_t scratch[kTopkStaticBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t topk_static_workspace(void **ptr, size_t *bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        // this device's copy of the array (host code must not use its name as an address)
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = kTopkStaticBytes;
+    return hipSuccess;
 }
 
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k, int32_t *idx,
