@@ -36,6 +36,7 @@
 //     tile through ds_read_b64_tr_b16 transposed reads.
 // FP8 rows (E4M3 + per-row scale) are gathered as bytes, expanded to bf16 in
 // LDS exactly, and their scale is applied to the logits and to P in fp32.
+#include <type_traits>
 #include <utility>
 
 #include "dsa_device.h"
@@ -595,6 +596,24 @@ __device__ __forceinline__ float sum_over_row_groups(float x) {
     return x + __shfl_xor(x, 32);
 }
 
+// Eight E4M3 codes -> eight bf16 values (exact), in order.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(const uint2 v) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Transposed 8-byte LDS read (measured lane layout): within each 16-lane group,
+// lane 2 r + h supplies 8 bytes (row r, columns 8 h .. +7 of an 8 x 16 byte
+// block) and lane i receives column i, rows 0..7 as bytes 0..7.
+__device__ __forceinline__ uint2 lds_tr8(const uint8_t *p) {
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(const_cast<uint8_t *>(p)));
+    return make_uint2((uint32_t)v.x, (uint32_t)v.y);
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256, 1) void sparse_mla_hg_kernel(
     const uint16_t *__restrict__ q, const void *__restrict__ kv_cache, const float *__restrict__ kv_scale,
@@ -604,14 +623,15 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_hg_kernel(
     constexpr int kCols = FP8 ? 9 : 18;                 // 64-byte column blocks copied per sub-tile
     constexpr int kC = kCols + (FP8 ? 1 : 0);           // copy instructions per sub-tile (FP8: + the row scales)
     constexpr int kLookK = 4, kLookV = 4;               // operand fragments in flight (register rings)
+    // Ring of sub-tile stages per wave: bf16 rows double-buffered (the next copies go
+    // into the stage being computed, block by block after its last read), FP8 codes
+    // in 4 stages with 3 sub-tiles in flight (copies go into the stage computed last).
+    constexpr int kStages = FP8 ? 4 : 2;
     constexpr int kStageB = FP8 ? kF8SubB : kSubB;
-    // sub_a / sub_b: the double buffer (bf16 rows, or FP8 codes expanded into sub_x)
+    constexpr int kWaitN = FP8 ? 2 * kC : kC;           // copies issued after a sub-tile's, at its wait
     __shared__ __attribute__((aligned(16))) int32_t slots[4][kHgRowsPerWave];
-    __shared__ __attribute__((aligned(16))) uint8_t sub_a[4][kStageB];
-    __shared__ __attribute__((aligned(16))) uint8_t sub_b[4][kStageB];
-    __shared__ __attribute__((aligned(16))) uint8_t sub_x[FP8 ? 4 : 1][FP8 ? kSubB : 16];
-    __shared__ __attribute__((aligned(16))) float fs_a[FP8 ? 4 : 1][64];   // FP8 row scales of the sub-tile in sub_a
-    __shared__ __attribute__((aligned(16))) float fs_b[FP8 ? 4 : 1][64];
+    __shared__ __attribute__((aligned(16))) uint8_t stages[4][kStages][kStageB];   // also the merge buffer
+    __shared__ __attribute__((aligned(16))) float fscale[FP8 ? 4 : 1][FP8 ? kStages : 1][64];   // FP8 row scales
     __shared__ float stat_m[4][32], stat_l[4][32];
 
     const int lane = threadIdx.x & 63;
@@ -659,21 +679,26 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_hg_kernel(
     __builtin_amdgcn_wave_barrier();
     const int n_sub = (n_w + kSub - 1) / kSub;
 
-    // ---- copies of sub-tile j (16 rows).  Copy instruction c moves column block c:
-    // lane l takes row l / 4 and the 16-byte piece l % 4 of the block, which for bf16
-    // rows holds chunk 4 c + ((l % 4) ^ swz(l / 4)) (swz(l / 4) = (l / 16) % 4).
+    // ---- copies of sub-tile j (16 rows).  Copy instruction c moves column block c
+    // (64 bytes of each row): lane l takes row l / 4 and the 16-byte piece
+    // (l % 4) ^ swz(l / 4) of the block, so slot p of row r in LDS holds piece
+    // p ^ swz(r) (swz(l / 4) = (l / 16) % 4).
     const uint8_t *kvb = reinterpret_cast<const uint8_t *>(kv_cache);
     constexpr int kRowBytes = FP8 ? kDk : kRowB;
-    const int piece = FP8 ? (lane & 3) : ((lane & 3) ^ ((lane >> 4) & 3));
+    const int piece = (lane & 3) ^ ((lane >> 4) & 3);
     auto slot_of = [&](int r) -> int64_t { return slots[wave][r < n_w ? r : 0]; };
+    auto copy_src = [&](int j) { return kvb + slot_of(16 * j + (lane >> 2)) * kRowBytes + 16 * piece; };
+    auto copy_col = [&](auto cc, const uint8_t *src, uint8_t *dst) {   // column block c
+        constexpr int c = decltype(cc)::value;
+        g2lds16<64 * c>(src, lds_addr(dst) + c * (kSubColB - 64));
+    };
     auto copies = [&](int j, uint8_t *dst, float *sdst) {
-        const uint8_t *src = kvb + slot_of(16 * j + (lane >> 2)) * kRowBytes + 16 * piece;
-        static_for<kCols>([&](auto cc) {
-            constexpr int c = decltype(cc)::value;
-            g2lds16<64 * c>(src, lds_addr(dst) + c * (kSubColB - 64));
-        });
+        const uint8_t *src = copy_src(j);
+        static_for<kCols>([&](auto cc) { copy_col(cc, src, dst); });
         if constexpr (FP8) g2lds4<0>(kv_scale + slot_of(16 * j + (lane & 15)), lds_addr(sdst));
     };
+    auto stage_of = [&](int s_) { return &stages[wave][s_][0]; };
+    auto scale_of = [&](int s_) { return &fscale[FP8 ? wave : 0][FP8 ? s_ : 0][0]; };
 
     // ---- Q^T of the group's heads (B operands): head 32 grp + 16 hh + l % 16, dims
     // 32 ks + 8 (l / 16) .. +8 (a head past h reads the last head; never stored)
@@ -689,43 +714,33 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_hg_kernel(
         }
     };
 
-    // Per-lane LDS offsets within a sub-tile.  K fragment of k-step ks: row l % 16,
-    // chunk l / 16 of column block ks.  V^T fragment of dim tile dt (lo / hi): lane
-    // i16 of a 16-lane group supplies row 8 g + 4 hi + i16 / 4 at dims
-    // 32 dt + 16 hd + 4 (i16 % 4), so the transposed reads give lane l the rows
-    // 8 (l / 32) .. +7 of dim 32 dt + l % 32 (the K order of the B operand below).
-    const int k_off = 64 * l16 + 16 * (q4 ^ swz(l16));
-    int v_off[2];
+    // Per-lane LDS offsets within a stage.
+    // bf16 K fragment of k-step ks: row l % 16, chunk l / 16 of column block ks.
+    // bf16 V^T fragment of dim tile dt (lo / hi): lane i16 of a 16-lane group
+    // supplies row 8 g + 4 hi + i16 / 4 at dims 32 dt + 16 hd + 4 (i16 % 4), so the
+    // transposed reads give lane l rows 8 (l / 32) .. +7 of dim 32 dt + l % 32.
+    // FP8 K fragment of k-step ks: row l % 16, codes 32 ks + 8 (l / 16) .. +8, i.e.
+    // column block ks / 2, piece 2 (ks % 2) + (l / 16) / 2, half (l / 16) % 2.
+    // FP8 V^T fragment of dim tile dt: lane 2 r + h of group G = l / 16 supplies row
+    // 8 (G / 2) + r, codes 32 dt + 16 (G % 2) + 8 h .. +8 (column block dt / 2,
+    // piece 2 (dt % 2) + G % 2), so the transposed read gives lane l rows
+    // 8 (l / 32) .. +7 of dim 32 dt + l % 32.
+    int k_off[2], v_off[2];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-        const int r = 8 * g + 4 * hi + (l16 >> 2), cq = 2 * hd + ((l16 >> 1) & 1);
-        v_off[hi] = 64 * r + 16 * (cq ^ swz(r)) + 8 * (l16 & 1);
-    }
-
-    // FP8: expand the staged codes of this wave's sub-tile into bf16 rows (exact).
-    // Staged column block c holds, in lane l's 16 bytes, codes 64 c + 16 (l % 4) ..
-    // +16 of row l / 4.
-    auto expand = [&](const uint8_t *src, uint8_t *dst) {
-        if constexpr (FP8) {
-            const int r = lane >> 2;
-#pragma unroll 3
-            for (int c = 0; c < 9; ++c) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(&src[c * 1024 + 16 * lane]);
-                const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-                uint32_t o8[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o8[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[e], 1.0f, false));
-                    o8[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wds[e], 1.0f, true));
-                }
-                const int ch = 8 * c + 2 * (lane & 3);   // bf16 chunks ch, ch + 1 (8 dims each)
-                *reinterpret_cast<uint4 *>(&dst[(ch >> 2) * kSubColB + 64 * r + 16 * ((ch & 3) ^ swz(r))]) =
-                    make_uint4(o8[0], o8[1], o8[2], o8[3]);
-                *reinterpret_cast<uint4 *>(&dst[((ch + 1) >> 2) * kSubColB + 64 * r + 16 * (((ch + 1) & 3) ^ swz(r))]) =
-                    make_uint4(o8[4], o8[5], o8[6], o8[7]);
-            }
+        for (int par = 0; par < 2; ++par) {
+            k_off[par] = 64 * l16 + 16 * ((2 * par + (q4 >> 1)) ^ swz(l16)) + 8 * (q4 & 1);
+            const int r = 8 * (q4 >> 1) + (l16 >> 1), pc = 2 * par + (q4 & 1);
+            v_off[par] = 64 * r + 16 * (pc ^ swz(r)) + 8 * (l16 & 1);
         }
-    };
+    } else {
+        k_off[0] = k_off[1] = 64 * l16 + 16 * (q4 ^ swz(l16));
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+            const int r = 8 * g + 4 * hi + (l16 >> 2), cq = 2 * hd + ((l16 >> 1) & 1);
+            v_off[hi] = 64 * r + 16 * (cq ^ swz(r)) + 8 * (l16 & 1);
+        }
+    }
 
     const float c2 = sm_scale * kLog2e;               // logits in log2 units: c2 * (q . k)
     // O^T accumulators: o[dt][i] holds dim 32 dt + 8 (i / 4) + 4 g + i % 4 of head 32 grp + l % 32
@@ -741,48 +756,71 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_hg_kernel(
 
     while (again) {
         again = false;
-        // one sub-tile: returns true when this wave must start over with a raised reference
-        auto step = [&](const int j, uint8_t *cur, float *fcur) -> bool {
-            wave_wait_loads<kC>();                    // sub-tile j landed (j + 1's copies may still fly)
-            const uint8_t *tile = cur;
-            if constexpr (FP8) {
-                expand(cur, sub_x[wave]);
-                tile = sub_x[wave];
-            }
+        // one sub-tile in stage S: returns true when this wave must start over with a
+        // raised reference
+        auto step = [&](auto sc_, const int j) -> bool {
+            constexpr int S = decltype(sc_)::value;
+            uint8_t *cur = stage_of(S);
+            wave_wait_loads<kWaitN>();                // sub-tile j landed
             float sc[4], sl[4];                        // FP8: row scale, and scale x c2, of rows 4 q4 + i
+            const uint8_t *nsrc = nullptr;
             if constexpr (FP8) {
-                const float4 f = *reinterpret_cast<const float4 *>(&fcur[4 * q4]);
+                const float4 f = *reinterpret_cast<const float4 *>(scale_of(S) + 4 * q4);
                 sc[0] = f.x; sc[1] = f.y; sc[2] = f.z; sc[3] = f.w;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sl[i] = sc[i] * c2;
-            }
-            if constexpr (FP8) {
-                // the staged codes and scales are read before the copies replace them
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                copies(j + 2 < n_sub ? j + 2 : n_sub - 1, cur, fcur);
+                // sub-tile j + 3 goes into the stage computed last (its reads are done)
+                constexpr int SN = (S + 3) % 4;
+                copies(j + 3 < n_sub ? j + 3 : n_sub - 1, stage_of(SN), scale_of(SN));
+            } else {
+                // sub-tile j + 2 goes into this stage column block by column block,
+                // each right after the block's last read (the rope blocks 16, 17 after
+                // the S^T MFMAs, block dt after the O^T MFMA of dim tile dt), spread
+                // over the MFMAs instead of issued in one burst
+                nsrc = copy_src(j + 2 < n_sub ? j + 2 : n_sub - 1);
             }
             const int lim = n_w - 16 * j - 4 * q4;    // element i is a selected row iff i < lim
             const bool partial = 16 * j + 16 > n_w;
 
             // S^T for both head halves over 18 k-steps; K fragments kLookK ahead
+            using KFrag = std::conditional_t<FP8, uint2, uint4>;
+            using VFrag = std::conditional_t<FP8, uint2, uint4>;
+            auto kload = [&](int ks) -> KFrag {
+                return *reinterpret_cast<const KFrag *>(cur + (FP8 ? (ks >> 1) : ks) * kSubColB + k_off[ks & 1]);
+            };
+            auto kfrag = [&](const KFrag &v) -> bf16x8 {
+                if constexpr (FP8) return fp8x8_to_bf16(v);
+                else return __builtin_bit_cast(bf16x8, v);
+            };
+            auto vload = [&](int dt) -> VFrag {
+                if constexpr (FP8) {
+                    return lds_tr8(cur + (dt >> 1) * kSubColB + v_off[dt & 1]);
+                } else {
+                    const uint8_t *p = cur + dt * kSubColB;
+                    const bf16x4 lo = lds_tr16(p + v_off[0]), hi = lds_tr16(p + v_off[1]);
+                    return __builtin_bit_cast(uint4, bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                }
+            };
+            auto vfrag = [&](const VFrag &v) -> bf16x8 {
+                if constexpr (FP8) return fp8x8_to_bf16(v);
+                else return __builtin_bit_cast(bf16x8, v);
+            };
             f32x4 s[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-            uint4 kr[kLookK];
-            auto kload = [&](int ks) { return *reinterpret_cast<const uint4 *>(tile + ks * kSubColB + k_off); };
+            KFrag kr[kLookK];
+            VFrag vr[kLookV];
 #pragma unroll
             for (int f = 0; f < kLookK; ++f) kr[f] = kload(f);
-            bf16x4 vlo[kLookV], vhi[kLookV];
-            auto vload = [&](int dt, bf16x4 &lo, bf16x4 &hi) {
-                const uint8_t *p = tile + dt * kSubColB;
-                lo = lds_tr16(p + v_off[0]);
-                hi = lds_tr16(p + v_off[1]);
-            };
             static_for<kK32>([&](auto kc) {
                 constexpr int ks = decltype(kc)::value;
-                const bf16x8 a = __builtin_bit_cast(bf16x8, kr[ks % kLookK]);
+                const bf16x8 a = kfrag(kr[ks % kLookK]);
                 if constexpr (ks + kLookK < kK32) kr[ks % kLookK] = kload(ks + kLookK);
-                else vload(ks + kLookK - kK32, vlo[ks + kLookK - kK32], vhi[ks + kLookK - kK32]);
+                else vr[ks + kLookK - kK32] = vload(ks + kLookK - kK32);
                 s[0] = mfma16_bf16(a, qf[0][ks], s[0]);
                 s[1] = mfma16_bf16(a, qf[1][ks], s[1]);
+                if constexpr (!FP8 && ks == kK32 - 1) {
+                    copy_col(std::integral_constant<int, 16>{}, nsrc, cur);
+                    copy_col(std::integral_constant<int, 17>{}, nsrc, cur);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
 
@@ -829,28 +867,32 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_hg_kernel(
             // O^T += V^T P^T over the 16 dim tiles; V^T fragments kLookV ahead
             static_for<16>([&](auto dc) {
                 constexpr int dt = decltype(dc)::value;
-                const bf16x4 lo = vlo[dt % kLookV], hi = vhi[dt % kLookV];
-                if constexpr (dt + kLookV < 16) vload(dt + kLookV, vlo[dt % kLookV], vhi[dt % kLookV]);
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                if constexpr (dt == 0) asm volatile("s_nop 4");   // pb was just written by VALU code
-                mfma32_bf16_acc(o[dt], a, pb);
+                const bf16x8 a = vfrag(vr[dt % kLookV]);
+                if constexpr (dt + kLookV < 16) vr[dt % kLookV] = vload(dt + kLookV);
+                // wait states: pb (and, FP8, the converted V^T fragment) were just written by VALU code
+                if constexpr (dt == 0 || FP8) asm volatile("s_nop 4");
+                mfma32_bf16_acc(o[dt], a, pb);                    // its operand reads of block dt are done
+                if constexpr (!FP8) copy_col(dc, nsrc, cur);
                 __builtin_amdgcn_sched_barrier(0);
             });
-            if constexpr (!FP8) {
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // every read of this buffer has returned
-                copies(j + 2 < n_sub ? j + 2 : n_sub - 1, cur, fcur);
-            }
             return __ballot(fmaxf(xmax[0], xmax[1]) > kHeadroom) != 0;
         };
-        copies(0, sub_a[wave], fs_a[FP8 ? wave : 0]);
-        copies(1 < n_sub ? 1 : 0, sub_b[wave], fs_b[FP8 ? wave : 0]);
+        // prologue: the sub-tiles in flight when step 0 starts (bf16: 0, 1; FP8: 0, 1, 2)
+        static_for<FP8 ? kStages - 1 : kStages>([&](auto sc_) {
+            constexpr int S = decltype(sc_)::value;
+            copies(S < n_sub ? S : n_sub - 1, stage_of(S), scale_of(S));
+        });
         if (first_attempt) {
             load_q();
             __builtin_amdgcn_s_waitcnt(0);            // q complete before the row loop (see the kernel above)
         }
-        for (int j = 0; j < n_sub; j += 2) {
-            if (step(j, sub_a[wave], fs_a[FP8 ? wave : 0])) { again = true; break; }
-            if (j + 1 < n_sub && step(j + 1, sub_b[wave], fs_b[FP8 ? wave : 0])) { again = true; break; }
+        for (int j = 0; j < n_sub; j += kStages) {
+            if (step(std::integral_constant<int, 0>{}, j)) { again = true; break; }
+            if (j + 1 < n_sub && step(std::integral_constant<int, 1>{}, j + 1)) { again = true; break; }
+            if constexpr (kStages == 4) {
+                if (j + 2 < n_sub && step(std::integral_constant<int, 2>{}, j + 2)) { again = true; break; }
+                if (j + 3 < n_sub && step(std::integral_constant<int, 3>{}, j + 3)) { again = true; break; }
+            }
         }
         wave_wait_loads<0>();                         // nothing of this attempt is in flight
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // the last O^T MFMA has written back
@@ -896,7 +938,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_hg_kernel(
     // rounds of 4 dim tiles: every wave writes its scaled partials of the round's
     // tiles, wave w sums tile 4 round + w over the waves.  Float4 e of lane l sits at
     // float4 index 4 l + ((e + l / 4) % 4) of a tile block: conflict-free.
-    float4 *mbuf = reinterpret_cast<float4 *>(FP8 ? &sub_x[0][0] : &sub_a[0][0]);   // [wave][tile][64 lanes x 4]
+    float4 *mbuf = reinterpret_cast<float4 *>(&stages[0][0][0]);   // [wave][tile][64 lanes x 4]
     auto slot4 = [&](int w, int d, int e) { return (w * 4 + d) * 256 + 4 * lane + ((e + (lane >> 2)) & 3); };
 #pragma unroll
     for (int round = 0; round < 4; ++round) {
