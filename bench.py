@@ -309,24 +309,47 @@ def decode_bytes(inp, k, h, kv_row_bytes=1152):
 
 
 # ---------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(inp, cfg, n_rows):
+def cpu_model():
+    """The host CPU's model name (first /proc/cpuinfo entry), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_rows(inp, cfg, rows, threads):
+    """Seconds the oracle takes for the full indexer row, top-k and sparse MLA of each row."""
     import oracle
-    rows = np.linspace(0, cfg.L - 1, n_rows).round().astype(np.int64)
     u8 = lambda t: t.detach().cpu().contiguous().numpy().view(np.uint8)
     b16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     iq, iqs, w = u8(inp.iq[rows]), inp.iq_scale[rows].cpu().numpy(), inp.w[rows].cpu().numpy()
     ik, iks = u8(inp.ik), inp.ik_scale.cpu().numpy()
     q, kv = b16(inp.q[rows]), b16(inp.kv)
     pos = rows.astype(np.int32)
-    threads = os.cpu_count() or 1
     t0 = time.perf_counter()
     sc = oracle.indexer_scores(iq, iqs, w, ik, iks, pos, ld=cfg.L, n_threads=threads)
     idx = oracle.topk(sc, pos, cfg.k, n_threads=threads)
     oracle.sparse_mla(q, kv, idx, SM_SCALE, n_threads=threads)
-    dt = time.perf_counter() - t0
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(inp, cfg, n_rows, n_rows_single=48):
+    """The oracle on the host cores: all threads over n_rows evenly spaced query
+    rows of the 32K prefill, and one thread over n_rows_single of them."""
+    threads = os.cpu_count() or 1
+    rows = np.linspace(0, cfg.L - 1, n_rows).round().astype(np.int64)
+    dt = _oracle_rows(inp, cfg, rows, threads)
+    rows1 = np.linspace(0, cfg.L - 1, n_rows_single).round().astype(np.int64)
+    dt1 = _oracle_rows(inp, cfg, rows1, 1)
     return {"value": n_rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_rows} evenly spaced query rows of the 32K prefill (positions 0..{cfg.L - 1}), full "
-                      f"indexer row + top-k + sparse MLA each, {dt:.1f} s wall on {threads} threads"}
+                      f"indexer row + top-k + sparse MLA each, {dt:.1f} s wall on {threads} threads",
+            "single_thread": {"value": n_rows_single / dt1, "unit": "tokens/s", "seconds": dt1,
+                              "sample": f"{n_rows_single} evenly spaced rows of the same prefill on 1 thread"},
+            "cpu_model": cpu_model()}
 
 
 # ---------------------------------------------------------------------------- all configs

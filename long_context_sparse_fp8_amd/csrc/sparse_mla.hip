@@ -1040,16 +1040,18 @@ hipError_t launch_mla_prefill(const MlaArgs &a, hipStream_t stream) {
 static int mla_head_groups(int32_t h) { return (h + 31) / 32; }
 
 int mla_decode_auto_splits(int32_t n_q, int32_t h, int32_t k) {
-    // One workgroup per (query, 32 heads) when that alone gives at least half a
+    // One workgroup per (query, 32 heads) when that gives between half and all of a
     // 256-CU device one workgroup each (64 queries x 128 heads: 256 workgroups):
-    // nothing leaves the chip but the output.  Fewer queries split the index list
-    // as well, each split writing an fp32 partial output that a second launch
-    // merges: about one workgroup per CU (every split re-reads the query's q
-    // block and writes and re-reads a 128 x 512 fp32 partial).
-    if ((int64_t)n_q * mla_head_groups(h) >= 128) return 1;
-    int s = 2;
+    // nothing leaves the chip but the output.  More workgroups would run in two
+    // rounds (128 queries: 164 us against 120 us with 2 splits).  Otherwise the
+    // index list is split, each split writing an fp32 partial output that a second
+    // launch merges: about one workgroup per CU (every split re-reads the query's
+    // q block and writes and re-reads a 128 x 512 fp32 partial).
+    const int64_t wg = (int64_t)n_q * mla_head_groups(h);
+    if (wg >= 128 && wg <= 256) return 1;
+    int s = 1;
     while (s < 32 && (int64_t)n_q * s < 256 && k / (2 * s) >= 2 * kTile) s *= 2;
-    return s;
+    return s > 1 ? s : 2;
 }
 
 size_t mla_decode_ws_bytes(int32_t n_q, int32_t h, int32_t n_splits) {
