@@ -7,7 +7,8 @@ token-granular cache with shuffled slots):
     cache stores -> indexer scores -> top-k -> sparse MLA prefill
 reported as prefill tokens/s.  Second figure: one decode step for 64
 sequences with contexts drawn uniformly from [32768, 131072] (one query
-each): cache stores -> indexer -> top-k -> sparse MLA decode, in us/step.
+each): cache stores -> indexer + top-k (the fused call) -> sparse MLA
+decode, in us/step, and the same step with the indexer and top-k as two calls.
 
 All inputs are seeded synthetic tensors generated on the GPU before timing.
 Each stage is bracketed by HIP events on the stream the kernels run on; the
@@ -240,17 +241,39 @@ def run_decode_step(cfg, inp, caches, newest, ds, timer=None):
     e = t("store")
     P.store_tokens(caches, newest["ik"], newest["ik_scale"], newest["ik_slot"], newest["kv"], newest["kv_slot"])
     if e: e.record()
-    e = t("indexer")
-    dsa.indexer_scores(inp.iq, inp.iq_scale, inp.w, caches.key_cache, caches.key_scale, inp.page_table, inp.q_seq,
-                       inp.q_pos, ds.scores)
-    if e: e.record()
-    e = t("topk")
-    dsa.topk(ds.scores, inp.q_pos, cfg.k, ds.idx, ws=ds.topk_ws)
-    if e: e.record()
+    if ds.fused_ws is not None:            # fused indexer -> top-k: one call, one stage
+        e = t("indexer_topk")
+        dsa.indexer_topk(inp.iq, inp.iq_scale, inp.w, caches.key_cache, caches.key_scale, inp.page_table, inp.q_seq,
+                         inp.q_pos, ds.scores, cfg.k, ds.idx, ds.fused_ws)
+        if e: e.record()
+    else:
+        e = t("indexer")
+        dsa.indexer_scores(inp.iq, inp.iq_scale, inp.w, caches.key_cache, caches.key_scale, inp.page_table,
+                           inp.q_seq, inp.q_pos, ds.scores)
+        if e: e.record()
+        e = t("topk")
+        dsa.topk(ds.scores, inp.q_pos, cfg.k, ds.idx, ws=ds.topk_ws)
+        if e: e.record()
     e = t("mla")
     dsa.sparse_mla_decode(inp.q, caches.kv_cache, inp.kv_slot_table, inp.q_seq, ds.idx, SM_SCALE, ds.out, ds.lse,
                           kv_scale=caches.kv_scale, n_splits=ds.n_splits, ws=ds.ws)
     if e: e.record()
+
+
+def decode_kernels(db, stages):
+    """Achieved HBM rate of each decode stage from its algorithmic bytes (a fused
+    indexer -> top-k stage carries the bytes of both)."""
+    parts = ([("indexer_topk", db["indexer_bytes"] + db["topk_bytes"], "indexer_topk")] if "indexer_topk" in stages
+             else [("indexer", db["indexer_bytes"], "indexer"), ("topk", db["topk_bytes"], "topk")])
+    parts.append(("sparse_mla_decode", db["mla_bytes"], "mla"))
+    out = {}
+    for name, nbytes, st in parts:
+        gbs = nbytes / (stages[st] * 1e-3) / 1e9
+        out[name] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s", "us": stages[st] * 1e3,
+                     "frac": gbs / PEAK_HBM}
+    if "indexer" in out:
+        out["indexer"]["traffic"] = recorded_traffic("indexer_decode")
+    return out
 
 
 def time_decode(args, cfg, inp, caches, newest, ds):
@@ -258,7 +281,8 @@ def time_decode(args, cfg, inp, caches, newest, ds):
     for _ in range(args.warmup):
         run_decode_step(cfg, inp, caches, newest, ds)
     torch.cuda.synchronize()
-    timer = StageTimer(["store", "indexer", "topk", "mla"])
+    timer = StageTimer(["store", "indexer_topk", "mla"] if ds.fused_ws is not None else
+                       ["store", "indexer", "topk", "mla"])
     t0 = time.perf_counter()
     for _ in range(args.steps):
         run_decode_step(cfg, inp, caches, newest, ds, timer)
@@ -497,8 +521,7 @@ def sweep_configs(args, dev):
     db = decode_bytes(dinp, dcfg.k, dcfg.h)
     res["C4"] = {"batch": dcfg.decode_batch, "us_per_step": dwall * 1e6, "us_per_step_graph": gwall * 1e6,
                  "graph_matches_eager": gsame, "stages_us": {k2: v * 1e3 for k2, v in dst.items()},
-                 "indexer_frac_hbm": db["indexer_bytes"] / (dst["indexer"] * 1e-3) / 1e9 / PEAK_HBM,
-                 "mla_frac_hbm": db["mla_bytes"] / (dst["mla"] * 1e-3) / 1e9 / PEAK_HBM}
+                 "kernels": decode_kernels(db, dst)}
     res["C4"]["oracle"] = oracle_decode_rate(dinp, dcfg, n_seq=8)
     del caches, dinp, ds, kv_slot
     torch.cuda.empty_cache()
@@ -586,22 +609,21 @@ def main():
         dcfg, dinp, caches, newest, ds, kv_slot = setup_decode_c4(dev)
         dwall, dst = time_decode(args, dcfg, dinp, caches, newest, ds)
         db = decode_bytes(dinp, dcfg.k, dcfg.h)
-        dk = {
-            "indexer": {"bound": "hbm", "achieved": db["indexer_bytes"] / (dst["indexer"] * 1e-3) / 1e9,
-                        "peak": PEAK_HBM, "unit": "GB/s", "us": dst["indexer"] * 1e3},
-            "topk": {"bound": "hbm", "achieved": db["topk_bytes"] / (dst["topk"] * 1e-3) / 1e9, "peak": PEAK_HBM,
-                     "unit": "GB/s", "us": dst["topk"] * 1e3},
-            "sparse_mla_decode": {"bound": "hbm", "achieved": db["mla_bytes"] / (dst["mla"] * 1e-3) / 1e9,
-                                  "peak": PEAK_HBM, "unit": "GB/s", "us": dst["mla"] * 1e3},
-        }
-        for v in dk.values():
-            v["frac"] = v["achieved"] / v["peak"]
-        dk["indexer"]["traffic"] = recorded_traffic("indexer_decode")
+        dk = decode_kernels(db, dst)
         result["decode"] = {"workload": "decode: 64 sequences x 1 query, context ~ U[32768, 131072] "
                                         f"(mean {float(dinp.lens.float().mean()):.0f}), k=2048, bf16 latent cache",
                             "us_per_step": dwall * 1e6, "tokens_per_s": dcfg.decode_batch / dwall,
                             "stages_us": {k2: v * 1e3 for k2, v in dst.items()}, "kernels": dk}
         log(f"[bench] decode {dwall * 1e6:.1f} us/step; stages us {result['decode']['stages_us']}")
+        # the same step with the indexer and the top-k as two calls (rows split over workgroups)
+        ds_u = P.alloc_decode(dcfg.decode_batch, int(dinp.lens.max()), dcfg.k, dcfg.h, fused=False, device=dev)
+        uwall, ust = time_decode(args, dcfg, dinp, caches, newest, ds_u)
+        result["decode"]["unfused"] = {"us_per_step": uwall * 1e6, "stages_us": {k2: v * 1e3 for k2, v in ust.items()},
+                                       "kernels": decode_kernels(db, ust),
+                                       "idx_equal_to_fused": bool(torch.equal(ds_u.idx, ds.idx))}
+        log(f"[bench] decode, indexer and top-k as two calls: {uwall * 1e6:.1f} us/step; stages us "
+            f"{result['decode']['unfused']['stages_us']}")
+        del ds_u
         gwall, gsame = time_decode_graph(args, dcfg, dinp, caches, newest, ds)
         result["decode"]["us_per_step_graph"] = gwall * 1e6
         result["decode"]["graph_replay_matches_eager"] = gsame
@@ -615,12 +637,7 @@ def main():
         ds2 = P.alloc_decode(2 * dcfg.decode_batch, int(dinp.lens.max()), dcfg.k, dcfg.h, device=dev)
         dwall2, dst2 = time_decode(args, dcfg, dinp2, caches, newest2, ds2)
         db2 = decode_bytes(dinp2, dcfg.k, dcfg.h)
-        dk2 = {name: {"bound": "hbm", "achieved": db2[key] / (dst2[st] * 1e-3) / 1e9, "peak": PEAK_HBM, "unit": "GB/s",
-                      "us": dst2[st] * 1e3} for name, key, st in
-               (("indexer", "indexer_bytes", "indexer"), ("topk", "topk_bytes", "topk"),
-                ("sparse_mla_decode", "mla_bytes", "mla"))}
-        for v in dk2.values():
-            v["frac"] = v["achieved"] / v["peak"]
+        dk2 = decode_kernels(db2, dst2)
         result["decode_mtp2"] = {
             "workload": "the decode step above with 2 query tokens per sequence (positions N-2, N-1): 128 queries",
             "us_per_step": dwall2 * 1e6, "tokens_per_s": 2 * dcfg.decode_batch / dwall2,

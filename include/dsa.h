@@ -180,6 +180,43 @@ size_t dsa_topk_workspace_size(int32_t n_q, int64_t max_len, int32_t k);
 dsa_status dsa_topk(const float *scores, int64_t scores_ld, const int32_t *q_pos, int32_t n_q, int32_t k,
                     int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Stages 1 + 2 fused (decode form)
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the workspace of dsa_indexer_topk for n_q queries: a block of
+ * 106,560 bytes per query (query t's at byte t * 106560, so a call with fewer
+ * queries uses a prefix of a larger workspace): 8256 bytes that must be zero
+ * (the row's key histogram and the selection's counters), then 96 KiB of
+ * scratch (the row's bitmap of kept indices and its candidate list). */
+size_t dsa_indexer_topk_workspace_size(int32_t n_q);
+
+/* dsa_indexer_scores followed by dsa_topk, with the selection's first pass
+ * fused into the scorer (the fused indexer -> top-k mode the SGLang DeepSeek
+ * V3.2 usage guide's MI350/MI355 recipe names): every scoring workgroup counts
+ * the order-preserving keys of the scores it writes in a histogram of their
+ * top 11 bits and adds it to its row's histogram in `ws` with integer atomics
+ * (the sum is order-independent, so results stay deterministic).  The
+ * selection then knows each row's threshold bin before reading a score: it
+ * reads every row once, in parts of 32K scores on separate workgroups, and the
+ * workgroup that finishes a row's last part completes that row.  Arguments,
+ * layouts and results are those of the two calls (scores are written as by
+ * dsa_indexer_scores, idx as by dsa_topk, bit-identical to them).
+ *   ws  at least dsa_indexer_topk_workspace_size(n_q) bytes of device memory,
+ *       16-byte aligned, ZERO before the first call; every successful call
+ *       leaves it as the next call needs it (the selection clears the regions
+ *       that must be zero), so one zeroed workspace serves every later call,
+ *       also in a replayed HIP graph.  Calls that use one workspace must not
+ *       overlap.  After a DSA_ERR_HIP return it must be zeroed again.
+ * Supported: the decode form, n_q <= 256 (DSA_ERR_UNSUPPORTED above: use the
+ * two calls); otherwise as dsa_indexer_scores and dsa_topk. */
+dsa_status dsa_indexer_topk(const uint8_t *q_fp8, const float *q_scale, const float *w, int64_t w_ld,
+                            const uint8_t *key_cache, const float *key_scale_cache, int64_t n_pages,
+                            const int32_t *page_table, int64_t pt_ld,
+                            const int32_t *q_seq, const int32_t *q_pos, int32_t n_q, int32_t h_i, int32_t d_i,
+                            float *scores, int64_t scores_ld, int32_t k, int32_t *idx, void *ws, size_t ws_bytes,
+                            void *stream);
+
 /* dsa_topk for callers that cannot allocate (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation): the same selection
  * and result, with the split rows' survivors in a static device array of the

@@ -19,6 +19,7 @@ KV_FP8_E4M3 = 1
 PAGE = 64
 DK = 576
 DV = 512
+INDEXER_DECODE_MAX_Q = 256   # largest query count of the split-key (decode) scorer and the fused call
 
 _lib = None
 
@@ -55,6 +56,10 @@ def lib():
     L.dsa_topk_workspace_size.argtypes = [i32, i64, i32]
     L.dsa_topk.restype = ctypes.c_int
     L.dsa_topk.argtypes = [P, i64, P, i32, i32, P, P, sz, P]
+    L.dsa_indexer_topk_workspace_size.restype = sz
+    L.dsa_indexer_topk_workspace_size.argtypes = [i32]
+    L.dsa_indexer_topk.restype = ctypes.c_int
+    L.dsa_indexer_topk.argtypes = [P, P, P, i64, P, P, i64, P, i64, P, P, i32, i32, i32, P, i64, i32, P, P, sz, P]
     L.dsa_topk_static.restype = ctypes.c_int
     L.dsa_topk_static.argtypes = [P, i64, P, i32, i32, P, P]
     L.dsa_sparse_mla_prefill.restype = ctypes.c_int
@@ -157,6 +162,27 @@ def topk(scores, q_pos, k, idx, ws=None, stream=None):
     _check(lib().dsa_topk(_ptr(scores, torch.float32, "scores"), ld, _ptr(q_pos, torch.int32, "q_pos"), n_q, k,
                           _ptr(idx, torch.int32, "idx"), _ptr(ws, None, "ws") if need else None,
                           need, _stream(stream)))
+
+
+def indexer_topk_workspace_size(n_q):
+    return int(lib().dsa_indexer_topk_workspace_size(n_q))
+
+
+def indexer_topk(q_fp8, q_scale, w, key_cache, key_scale_cache, page_table, q_seq, q_pos, scores, k, idx, ws,
+                 w_shared=False, stream=None):
+    """indexer_scores then topk with the selection's first pass fused into the scorer (decode form,
+    n_q <= 256).  ws: uint8 device tensor of at least indexer_topk_workspace_size(n_q) bytes, zero
+    before the first call; every call leaves it ready for the next."""
+    n_q, h_i, d_i = q_fp8.shape
+    _check(lib().dsa_indexer_topk(_ptr(q_fp8, torch.uint8, "q_fp8"), _ptr(q_scale, torch.float32, "q_scale"),
+                                  _ptr(w, torch.float32, "w"), 0 if w_shared else h_i,
+                                  _ptr(key_cache, torch.uint8, "key_cache"),
+                                  _ptr(key_scale_cache, torch.float32, "key_scale_cache"), key_cache.shape[0],
+                                  _ptr(page_table, torch.int32, "page_table"), page_table.shape[1],
+                                  _ptr(q_seq, torch.int32, "q_seq"), _ptr(q_pos, torch.int32, "q_pos"),
+                                  n_q, h_i, d_i, _ptr(scores, torch.float32, "scores"), scores.shape[1], k,
+                                  _ptr(idx, torch.int32, "idx"), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+                                  _stream(stream)))
 
 
 def topk_static(scores, q_pos, k, idx, stream=None):

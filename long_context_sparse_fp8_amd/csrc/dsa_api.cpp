@@ -125,6 +125,55 @@ DSA_EXPORT dsa_status dsa_indexer_scores(const uint8_t *q_fp8, const float *q_sc
     return DSA_OK;
 }
 
+DSA_EXPORT size_t dsa_indexer_topk_workspace_size(int32_t n_q) {
+    return n_q > 0 ? dsa::fused_topk_ws_bytes(n_q) : 0;
+}
+
+DSA_EXPORT dsa_status dsa_indexer_topk(const uint8_t *q_fp8, const float *q_scale, const float *w, int64_t w_ld,
+                                       const uint8_t *key_cache, const float *key_scale_cache, int64_t n_pages,
+                                       const int32_t *page_table, int64_t pt_ld, const int32_t *q_seq,
+                                       const int32_t *q_pos, int32_t n_q, int32_t h_i, int32_t d_i, float *scores,
+                                       int64_t scores_ld, int32_t k, int32_t *idx, void *ws, size_t ws_bytes,
+                                       void *stream) {
+    REQUIRE(n_q >= 0, DSA_ERR_BAD_SHAPE, "dsa_indexer_topk: n_q = %d < 0", n_q);
+    REQUIRE(n_q <= dsa::kIndexerDecodeMaxQ, DSA_ERR_UNSUPPORTED,
+            "dsa_indexer_topk: n_q = %d > %d (the fused call is the decode form; use dsa_indexer_scores + dsa_topk)",
+            n_q, dsa::kIndexerDecodeMaxQ);
+    REQUIRE((h_i == 64 && d_i == 128) || (h_i == 16 && d_i == 64), DSA_ERR_UNSUPPORTED,
+            "dsa_indexer_topk: (h_i, d_i) = (%d, %d) not in {(16, 64), (64, 128)}", h_i, d_i);
+    REQUIRE(w_ld == 0 || w_ld >= h_i, DSA_ERR_BAD_SHAPE, "dsa_indexer_topk: w_ld = %lld (need 0 or >= h_i)",
+            (long long)w_ld);
+    REQUIRE(n_pages >= 0 && pt_ld >= 1, DSA_ERR_BAD_SHAPE, "dsa_indexer_topk: n_pages / pt_ld out of range");
+    REQUIRE(scores_ld >= 1, DSA_ERR_BAD_SHAPE, "dsa_indexer_topk: scores_ld = %lld < 1", (long long)scores_ld);
+    REQUIRE(scores_ld <= DSA_MAX_TOPK_ROW, DSA_ERR_UNSUPPORTED, "dsa_indexer_topk: scores_ld = %lld > %d",
+            (long long)scores_ld, DSA_MAX_TOPK_ROW);
+    REQUIRE(k >= 1 && k <= DSA_MAX_TOPK, DSA_ERR_UNSUPPORTED, "dsa_indexer_topk: k = %d not in [1, %d]", k,
+            DSA_MAX_TOPK);
+    if (n_q == 0) return DSA_OK;
+    REQUIRE_PTR(q_fp8);
+    REQUIRE_PTR(q_scale);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(key_cache);
+    REQUIRE_PTR(key_scale_cache);
+    REQUIRE_PTR(page_table);
+    REQUIRE_PTR(q_seq);
+    REQUIRE_PTR(q_pos);
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(idx);
+    const size_t need = dsa::fused_topk_ws_bytes(n_q);
+    REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "dsa_indexer_topk: ws_bytes = %zu < %zu needed", ws_bytes,
+            need);
+    REQUIRE_PTR(ws);
+    dsa::IndexerArgs a{q_fp8, q_scale, w, w_ld, key_cache, key_scale_cache, n_pages, page_table, pt_ld,
+                       q_seq, q_pos, n_q, h_i, d_i, scores, scores_ld, reinterpret_cast<uint32_t *>(ws)};
+    hipError_t e = dsa::launch_indexer(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "dsa_indexer_topk: scorer launch");
+    e = dsa::launch_topk_fused(scores, scores_ld, q_pos, n_q, k, idx, reinterpret_cast<uint32_t *>(ws),
+                               (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "dsa_indexer_topk: selection launch");
+    return DSA_OK;
+}
+
 DSA_EXPORT size_t dsa_topk_workspace_size(int32_t n_q, int64_t max_len, int32_t k) {
     if (n_q <= 0 || max_len <= 0 || k < 1 || k > DSA_MAX_TOPK || max_len > DSA_MAX_TOPK_ROW) return 0;
     return dsa::topk_ws_bytes(n_q, max_len, k);

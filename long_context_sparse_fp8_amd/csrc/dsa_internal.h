@@ -26,6 +26,22 @@ __host__ __device__ constexpr int idx_key_piece_offset(int key, int piece, int d
 // Top-k limits: k <= kTopkMaxK, score rows of at most kTopkMaxRow columns.
 constexpr int kTopkMaxK = 2048;
 constexpr int64_t kTopkMaxRow = 262144;
+// Workspace of the fused indexer -> top-k call: one block of kFusedRowStride
+// words per query row t (at t * kFusedRowStride, so calls with fewer rows use
+// a prefix of it), holding
+//   * kFusedRowWords words that must be zero before the call and are left zero
+//     by it: the row's first-digit histogram (order-preserving key bits
+//     31..21, built by the split-key scorer), then the selection's part
+//     ticket, candidate count and overflow flag;
+//   * scratch: the row's bitmap of kept indices and its candidate list.
+constexpr int kTopkHistBins = 2048;
+constexpr int kFusedRowWords = kTopkHistBins + 16;
+constexpr int kFusedCand = 8192;                                   // candidate list capacity per row
+constexpr int64_t kFusedScratchWords = kTopkMaxRow / 32 + 2 * kFusedCand;
+constexpr int64_t kFusedRowStride = kFusedRowWords + kFusedScratchWords;
+constexpr size_t fused_topk_ws_bytes(int32_t n_q) {
+    return (size_t)n_q * (size_t)kFusedRowStride * sizeof(uint32_t);
+}
 
 struct IndexerArgs {
     const uint8_t *q_fp8;
@@ -42,6 +58,7 @@ struct IndexerArgs {
     int32_t n_q, h_i, d_i;
     float *scores;
     int64_t scores_ld;
+    uint32_t *hist = nullptr;   // row t's histogram at hist + t * kFusedRowStride (zeroed): accumulated into
 };
 
 struct MlaArgs {
@@ -67,6 +84,11 @@ hipError_t launch_kv_store(const uint16_t *kv, const int64_t *slot, int32_t n, i
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream);
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k, int32_t *idx,
                        void *ws, size_t ws_bytes, hipStream_t stream);
+// Top-k of rows whose first-digit histograms the split-key scorer accumulated
+// in the fused workspace `ws` (fused_topk_ws_bytes(n_q) bytes, laid out as
+// above; the regions that must be zero are left zero).
+hipError_t launch_topk_fused(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k,
+                             int32_t *idx, uint32_t *ws, hipStream_t stream);
 // Workspace that lets dsa_topk split few long rows over several workgroups
 // (0 when it does not split at these sizes).
 size_t topk_ws_bytes(int32_t n_q, int64_t ld, int32_t k);

@@ -243,16 +243,24 @@ constexpr int kDecDepth = 1;                      // pages per wave in flight wh
 // stay in registers and are stored after its last page: stores and loads share
 // one completion counter, so a store between the page loads would make every
 // later wait also wait for it (measured: 20% of the scan).
-template <int H_I, int D_I>
+//
+// HIST (the fused indexer -> top-k call): every workgroup also counts the keys
+// of the scores it writes in an LDS histogram of the top-k's first digit (key
+// bits 31..21, two lane-interleaved copies) and adds its non-zero bins to the
+// row's histogram in `hist` with integer atomics (order-independent), so the
+// top-k starts from the finished histogram instead of a sweep over the row.
+template <int H_I, int D_I, bool HIST>
 __global__ __launch_bounds__(256, 2) void indexer_decode_kernel(
     const uint8_t *__restrict__ q_fp8, const float *__restrict__ q_scale, const float *__restrict__ w, int64_t w_ld,
     const uint8_t *__restrict__ key_cache, const float *__restrict__ key_scale, int64_t n_pages,
     const int32_t *__restrict__ page_table, int64_t pt_ld, const int32_t *__restrict__ q_seq,
-    const int32_t *__restrict__ q_pos, int32_t n_q, float *__restrict__ scores, int64_t ld, int pages_per_split) {
+    const int32_t *__restrict__ q_pos, int32_t n_q, float *__restrict__ scores, int64_t ld, int pages_per_split,
+    uint32_t *__restrict__ hist) {
     using S = IdxShape<H_I, D_I>;
     constexpr int NH = 32 * S::HT;                   // heads rounded up to MFMA row tiles
     __shared__ __attribute__((aligned(16))) uint8_t q_lds[2][NH * S::ROW];   // padded rows: conflict-free reads
     __shared__ __attribute__((aligned(16))) float w_lds[2][NH];
+    __shared__ __attribute__((aligned(16))) uint32_t h_lds[HIST ? 2 : 1][HIST ? 2 * kTopkHistBins : 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
     const int t = blockIdx.x;
     const int64_t max_page = (ld + kPage - 1) / kPage;
@@ -274,10 +282,14 @@ __global__ __launch_bounds__(256, 2) void indexer_decode_kernel(
         if (p_begin >= p_end) return;                // uniform over the workgroup
         if (n_pages <= 0) {                          // no page can be read: every score is NaN
 #pragma unroll
-            for (int j = 0; j < NQ; ++j)
-                for (int64_t key = p_begin * kPage + threadIdx.x;
-                     key < min(p_end * kPage, min((int64_t)pos[j] + 1, ld)); key += 256)
+            for (int j = 0; j < NQ; ++j) {
+                const int64_t k0 = p_begin * kPage, k1 = min(p_end * kPage, min((int64_t)pos[j] + 1, ld));
+                for (int64_t key = k0 + threadIdx.x; key < k1; key += 256)
                     scores[(int64_t)(t1 + j) * ld + key] = __builtin_nanf("");
+                if (HIST && threadIdx.x == 0 && k1 > k0)
+                    atomicAdd(&hist[(int64_t)(t1 + j) * kFusedRowStride + (f32_order_key(__builtin_nanf("")) >> 21)],
+                              (uint32_t)(k1 - k0));
+            }
             return;
         }
         // physical page of page p_begin + lane, -1 when absent or out of range
@@ -292,6 +304,9 @@ __global__ __launch_bounds__(256, 2) void indexer_decode_kernel(
         }
         // the queries' FP8 rows (heads past H_I zero) and weights
         __syncthreads();                             // a previous run's readers are done
+        if constexpr (HIST) {
+            for (int b = threadIdx.x; b < NQ * 2 * kTopkHistBins; b += 256) h_lds[b / (2 * kTopkHistBins)][b % (2 * kTopkHistBins)] = 0u;
+        }
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             for (int c = threadIdx.x; c < NH * S::CH; c += 256) {
@@ -391,7 +406,20 @@ __global__ __launch_bounds__(256, 2) void indexer_decode_kernel(
 #pragma unroll
             for (int m = 0; m < SLOTS; ++m) {
                 const int64_t key = (p_begin + wave + 4 * m) * kPage + lane;
-                if (key < k_end) srow[key] = sreg[j][m];
+                if (key < k_end) {
+                    srow[key] = sreg[j][m];
+                    if constexpr (HIST) atomicAdd(&h_lds[j][(f32_order_key(sreg[j][m]) >> 21) * 2 + (lane & 1)], 1u);
+                }
+            }
+        }
+        if constexpr (HIST) {
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                for (int b = threadIdx.x; b < kTopkHistBins; b += 256) {
+                    const uint32_t c = h_lds[j][2 * b] + h_lds[j][2 * b + 1];
+                    if (c != 0u) atomicAdd(&hist[(int64_t)(t1 + j) * kFusedRowStride + b], c);
+                }
             }
         }
     };
@@ -419,9 +447,14 @@ static hipError_t launch_indexer_t(const IndexerArgs &a, hipStream_t stream) {
         const int64_t row_pages = (a.scores_ld + kPage - 1) / kPage;
         const int64_t splits = (std::max(a.pt_ld, row_pages) + pps - 1) / pps;
         dim3 grid((unsigned)a.n_q, (unsigned)(splits > 0 ? splits : 1));
-        hipLaunchKernelGGL((indexer_decode_kernel<H_I, D_I>), grid, dim3(256), 0, stream, a.q_fp8, a.q_scale, a.w,
-                           a.w_ld, a.key_cache, a.key_scale, a.n_pages, a.page_table, a.pt_ld, a.q_seq, a.q_pos,
-                           a.n_q, a.scores, a.scores_ld, pps);
+        if (a.hist != nullptr)
+            hipLaunchKernelGGL((indexer_decode_kernel<H_I, D_I, true>), grid, dim3(256), 0, stream, a.q_fp8,
+                               a.q_scale, a.w, a.w_ld, a.key_cache, a.key_scale, a.n_pages, a.page_table, a.pt_ld,
+                               a.q_seq, a.q_pos, a.n_q, a.scores, a.scores_ld, pps, a.hist);
+        else
+            hipLaunchKernelGGL((indexer_decode_kernel<H_I, D_I, false>), grid, dim3(256), 0, stream, a.q_fp8,
+                               a.q_scale, a.w, a.w_ld, a.key_cache, a.key_scale, a.n_pages, a.page_table, a.pt_ld,
+                               a.q_seq, a.q_pos, a.n_q, a.scores, a.scores_ld, pps, nullptr);
     } else {
         constexpr int QPW = 2;
         const int nqb = (a.n_q + 4 * QPW - 1) / (4 * QPW);

@@ -71,6 +71,7 @@ struct TopkShape {
 template <int NT, int C>
 struct TopkSmem {
     using S = TopkShape<NT, C>;
+    static constexpr int kThreads = NT;
     union {
         uint32_t hist0[kBins0 * S::kCopies0];   // hist0[bin * kCopies0 + lane % kCopies0]
         struct {
@@ -87,8 +88,9 @@ struct TopkSmem {
 
 // Block-wide exclusive scan (all NT threads call it); returns the sum over
 // lower threads, `total` gets the block sum.
-template <int NT, int C>
-__device__ __forceinline__ uint32_t block_excl_scan(TopkSmem<NT, C> &sm, uint32_t a, uint32_t &total) {
+template <class SM>
+__device__ __forceinline__ uint32_t block_excl_scan(SM &sm, uint32_t a, uint32_t &total) {
+    constexpr int NT = SM::kThreads;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t ia = a;
 #pragma unroll
@@ -136,8 +138,8 @@ __device__ __forceinline__ void load_chunk(const float *row, int n, int c, uint3
 // holds the rem-th element.  Wave 0 only; the caller synchronises.  Kept out of
 // line: inlined, its reads get scheduled into the callers' loops and pin
 // registers for the whole kernel.
-template <int NT, int C>
-__device__ __noinline__ void pick_digit(TopkSmem<NT, C> &sm, int nb, uint32_t rem, bool desc) {
+template <class SM>
+__device__ __noinline__ void pick_digit(SM &sm, int nb, uint32_t rem, bool desc) {
     const int lane = threadIdx.x & 63;
     uint32_t c[8];   // lane owns 8 consecutive bins in scan order (nb <= 512)
     uint32_t tot = 0;
@@ -473,6 +475,338 @@ __global__ __launch_bounds__(NT, 1024 / NT) void topk_kernel(const float *__rest
     }
 }
 
+// ---------------------------------------------------------------- fused selection
+// The fused indexer -> top-k call.  The split-key scorer has accumulated each
+// row's first-digit histogram (key bits 31..21) in the workspace, so the
+// threshold bin b0 of a row, how many keys it holds and how many of them are
+// still needed are known before a score is read.  Two launches, each row read
+// once:
+//   PART (one workgroup per kFusedPart scores of a row; every part scans the
+//   same histogram and finds the same b0): the part's scores are loaded into
+//   registers; every key above b0 (at or above it when the bin is taken whole)
+//   sets its bit in the part's slice of the row's bitmap of kept indices, and
+//   the keys of bin b0 are appended to per-wave LDS lists (ballot and lane
+//   count: no atomics in the sweep), then copied to the row's candidate list
+//   in the workspace (one global atomic per wave reserves the range);
+//   MERGE (one workgroup per row): reads the bitmap and the candidates,
+//   finishes the radix select on the candidates (8-, 8- and 5-bit digits, then
+//   the index cut among keys equal to the threshold), adds the kept ones to the
+//   bitmap, writes the kept indices in ascending order and clears the row's
+//   histogram and counters for the next call.
+// When the threshold bin holds more keys than the list (a row of mostly equal
+// scores) or a wave's list overflows, MERGE finishes the select over the whole
+// row instead, re-reading it.  Everything is integer: the result is that of
+// topk_kernel.  (A single launch, whose last part workgroup merges, needs a
+// device-scope release fence per workgroup -- an L2 write-back -- that costs
+// more than the second launch.)
+constexpr int kFusedPartNT = 512;
+constexpr int kFusedC = 8;                                        // chunks of 4 NT scores per part
+constexpr int kFusedPart = kFusedC * 4 * kFusedPartNT;            // 16384 scores per part workgroup
+constexpr int kFusedWaveCand = 256;                               // per-wave LDS list of a part
+constexpr int kFusedMergeNT = 1024;
+// row header in the zero region, after the histogram
+constexpr int kHdrCand = kTopkHistBins, kHdrOverflow = kTopkHistBins + 1, kHdrB0 = kTopkHistBins + 2,
+              kHdrRem = kTopkHistBins + 3, kHdrFlags = kTopkHistBins + 4;
+static_assert(kFusedPart % 32 == 0, "parts cover whole bitmap words");
+static_assert(kHdrFlags < kFusedRowWords, "header inside the zero region");
+
+struct FusedPartSmem {
+    static constexpr int kThreads = kFusedPartNT;
+    uint32_t bitmap[kFusedPart / 32];
+    struct {
+        uint32_t key[kFusedWaveCand];
+        int32_t idx[kFusedWaveCand];
+    } list[kFusedPartNT / kWave];
+    uint32_t wsum[kFusedPartNT / kWave];
+    uint32_t sel_bin, sel_rem, sel_done, sel_cnt;
+};
+
+struct FusedMergeSmem {
+    static constexpr int kThreads = kFusedMergeNT;
+    uint32_t bitmap[kTopkMaxRow / 32];
+    struct {
+        uint32_t key[kFusedCand];
+        int32_t idx[kFusedCand];
+    } cand;
+    uint32_t hist[kBins * kCopies];
+    int32_t stage[kTopkMaxK];
+    uint32_t wsum[kFusedMergeNT / kWave];
+    uint32_t sel_bin, sel_rem, sel_done;
+};
+
+__device__ __forceinline__ int fused_row_len(const int32_t *q_pos, int t, int64_t ld) {
+    int64_t n = (int64_t)q_pos[t] + 1;
+    if (n > ld) n = ld;
+    if (n < 0) n = 0;
+    return (int)n;   // n <= ld <= kTopkMaxRow (checked by the API)
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kFusedPartNT, 2) void topk_fused_part_kernel(const float *__restrict__ scores,
+                                                                         int64_t ld,
+                                                                         const int32_t *__restrict__ q_pos,
+                                                                         int32_t k, uint32_t *__restrict__ ws) {
+    constexpr int NT = kFusedPartNT, C = kFusedC, kChunk = 4 * NT, R = kFusedWaveCand;
+    __shared__ __attribute__((aligned(16))) FusedPartSmem sm;
+    const int t = blockIdx.x, part = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = fused_row_len(q_pos, t, ld);
+    if (n <= k) return;                           // MERGE keeps every candidate
+    const int base = part * kFusedPart;
+    if (base >= n) return;
+    const int n_here = min(kFusedPart, n - base), nc = (n_here + kChunk - 1) / kChunk;
+    uint32_t *zr = ws + (int64_t)t * kFusedRowStride;
+    uint32_t *rbits = zr + kFusedRowWords;
+    uint32_t *rkey = rbits + kTopkMaxRow / 32;
+    int32_t *ridx = reinterpret_cast<int32_t *>(rkey + kFusedCand);
+    const float *row = scores + (int64_t)t * ld + base;
+
+    // the histogram first, then the part's raw scores: the scan below waits for
+    // the histogram only, while the scores are still on their way
+    constexpr int B = kTopkHistBins / NT;         // bins per thread (4), descending from the top
+    static_assert(B == 4, "one 16-byte histogram load per thread");
+    const uint4 hv = reinterpret_cast<const uint4 *>(zr)[kTopkHistBins / 4 - 1 - tid];
+    float x[C][4];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int i = min(c, nc - 1) * kChunk + 4 * tid;
+        if constexpr (VEC) {   // the row is 16-byte aligned; ceil4(n) <= ld
+            const float4 v = *reinterpret_cast<const float4 *>(row + min(i, ((n_here + 3) & ~3) - 4));
+            x[c][0] = v.x;
+            x[c][1] = v.y;
+            x[c][2] = v.z;
+            x[c][3] = v.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[c][e] = row[min(i + e, n_here - 1)];
+        }
+    }
+    // ---- the threshold bin b0 (bins scanned from the top)
+    if (tid == 0) {   // defaults for a histogram that does not hold the row (never for a zeroed workspace)
+        sm.sel_bin = 0u;
+        sm.sel_rem = (uint32_t)k;
+        sm.sel_done = 0u;
+        sm.sel_cnt = 0xFFFFFFFFu;
+    }
+    for (int w = tid; w < kFusedPart / 32; w += NT) sm.bitmap[w] = 0u;
+    {
+        const uint32_t cnt[B] = {hv.w, hv.z, hv.y, hv.x};   // bins 2047 - 4 tid - j
+        const uint32_t mine = (cnt[0] + cnt[1]) + (cnt[2] + cnt[3]);
+        uint32_t total;
+        uint32_t excl = block_excl_scan(sm, mine, total);   // (its barriers also order the clears above)
+        const uint32_t kk = (uint32_t)k;
+        if (excl < kk && excl + mine >= kk) {
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                if (excl < kk && excl + cnt[j] >= kk) {
+                    sm.sel_bin = (uint32_t)(kTopkHistBins - 1 - B * tid - j);
+                    sm.sel_rem = kk - excl;
+                    sm.sel_done = (excl + cnt[j] == kk) ? 1u : 0u;
+                    sm.sel_cnt = cnt[j];
+                }
+                excl += cnt[j];
+            }
+        }
+        __syncthreads();
+    }
+    const uint32_t b0 = sm.sel_bin;
+    const bool whole_bin = sm.sel_done != 0u;
+    const bool collect = !whole_bin && sm.sel_cnt <= (uint32_t)kFusedCand;
+    if (part == 0 && tid == 0) {                  // for MERGE (every part finds the same)
+        zr[kHdrB0] = b0;
+        zr[kHdrRem] = sm.sel_rem;
+        zr[kHdrFlags] = (whole_bin ? 1u : 0u) | (collect ? 2u : 0u);
+    }
+
+    // ---- sweep: bitmap slice of the keys above b0, per-wave lists of bin b0
+    uint32_t wfill = 0;                           // this wave's list length (uniform)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (c < nc) {
+            const int i0 = c * kChunk + 4 * tid;  // index within the part; its 4 keys share a bitmap word
+            uint32_t above = 0, mine = 0, key[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                key[e] = f32_order_key(x[c][e]);
+                const uint32_t bin = key[e] >> 21;
+                const bool v = i0 + e < n_here;
+                above |= (uint32_t)(v && (bin > b0 || (whole_bin && bin == b0))) << e;
+                mine |= (uint32_t)(v && collect && bin == b0) << e;
+            }
+            if (above != 0u) atomicOr(&sm.bitmap[i0 >> 5], above << (i0 & 31));
+            if (collect) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool me = ((mine >> e) & 1u) != 0u;
+                    const uint64_t m = __ballot(me);
+                    if (m != 0ull) {
+                        const uint32_t slot =
+                            wfill + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        if (me && slot < (uint32_t)R) {
+                            sm.list[wave].key[slot] = key[e];
+                            sm.list[wave].idx[slot] = base + i0 + e;
+                        }
+                        wfill += (uint32_t)__popcll(m);
+                    }
+                }
+            }
+        }
+    }
+    // this wave's list to the row's candidates (a wave reads back only its own list)
+    if (collect && wfill > 0u) {
+        uint32_t g0 = 0u;
+        if (lane == 0) g0 = wfill > (uint32_t)R ? 0u : atomicAdd(&zr[kHdrCand], wfill);
+        g0 = (uint32_t)__shfl((int)g0, 0);
+        if (wfill <= (uint32_t)R && g0 + wfill <= (uint32_t)kFusedCand) {
+            for (uint32_t j = lane; j < wfill; j += kWave) {
+                rkey[g0 + j] = sm.list[wave].key[j];
+                ridx[g0 + j] = sm.list[wave].idx[j];
+            }
+        } else if (lane == 0) {
+            atomicOr(&zr[kHdrOverflow], 1u);      // MERGE re-reads the row
+        }
+    }
+    __syncthreads();
+    {
+        const int w0 = base >> 5, nw = (n_here + 31) >> 5;
+        for (int w = tid; w < nw; w += NT) rbits[w0 + w] = sm.bitmap[w];
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kFusedMergeNT, 1) void topk_fused_merge_kernel(const float *__restrict__ scores,
+                                                                           int64_t ld,
+                                                                           const int32_t *__restrict__ q_pos,
+                                                                           int32_t k, int32_t *__restrict__ idx,
+                                                                           uint32_t *__restrict__ ws) {
+    constexpr int NT = kFusedMergeNT, kChunk = 4 * NT;
+    __shared__ __attribute__((aligned(16))) FusedMergeSmem sm;
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = fused_row_len(q_pos, t, ld);
+    uint32_t *zr = ws + (int64_t)t * kFusedRowStride;
+    int32_t *out = idx + (int64_t)t * k;
+    if (n <= k) {   // every candidate is kept
+        for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
+        for (int b = tid; b < kFusedRowWords; b += NT) zr[b] = 0u;
+        return;
+    }
+    const uint32_t *rbits = zr + kFusedRowWords;
+    const uint32_t *rkey = rbits + kTopkMaxRow / 32;
+    const int32_t *ridx = reinterpret_cast<const int32_t *>(rkey + kFusedCand);
+    const float *row = scores + (int64_t)t * ld;
+    const uint32_t b0 = zr[kHdrB0], flags = zr[kHdrFlags];
+    uint32_t rem = zr[kHdrRem];
+    const bool whole_bin = (flags & 1u) != 0u;
+    const bool use_list = (flags & 2u) != 0u && zr[kHdrOverflow] == 0u;
+    const uint32_t n_list = use_list ? min(zr[kHdrCand], (uint32_t)kFusedCand) : 0u;
+    const int nwords = (n + 31) >> 5;
+    for (int w = tid; w < nwords; w += NT) sm.bitmap[w] = rbits[w];
+    for (int j = tid; j < (int)n_list; j += NT) {
+        sm.cand.key[j] = rkey[j];
+        sm.cand.idx[j] = ridx[j];
+    }
+    __syncthreads();
+    // fn(key, index) over the keys still in play: the row's candidates, or the whole row re-read
+    auto each_live = [&](auto fn) {
+        if (use_list) {
+            for (int j = tid; j < (int)n_list; j += NT) fn(sm.cand.key[j], sm.cand.idx[j]);
+        } else {
+            const int ncr = (n + kChunk - 1) / kChunk;
+            for (int c = 0; c < ncr; ++c) {
+                uint32_t key[4];
+                load_chunk<NT, VEC>(row, n, c, key);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = c * kChunk + 4 * tid + e;
+                    if (i < n) fn(key[e], i);
+                }
+            }
+        }
+    };
+    uint32_t *hc = sm.hist + (lane & (kCopies - 1));
+    auto clear_hist = [&]() {
+        for (int i = tid; i < kBins * kCopies / 4; i += NT)
+            reinterpret_cast<uint4 *>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
+    };
+    bool done = whole_bin;
+    uint32_t prefix = b0 << 21, pmask = 0xFFE00000u;
+    if (!done) {   // digits 8, 8, 5 below the first 11 bits
+#pragma unroll 1
+        for (int pass = 0; pass < 3 && !done; ++pass) {
+            const int shift = pass == 0 ? 13 : (pass == 1 ? 5 : 0);
+            const int width = pass == 2 ? 5 : 8;
+            const uint32_t dmask = (1u << width) - 1u;
+            clear_hist();
+            __syncthreads();
+            each_live([&](uint32_t key, int) {
+                if ((key & pmask) == prefix) atomicAdd(&hc[((key >> shift) & dmask) * kCopies], 1u);
+            });
+            __syncthreads();
+            if (wave == 0) pick_digit(sm, 1 << width, rem, true);
+            __syncthreads();
+            prefix |= sm.sel_bin << shift;
+            pmask |= dmask << shift;
+            rem = sm.sel_rem;
+            done = sm.sel_done != 0u;
+            __syncthreads();
+        }
+    }
+    // keys with (key & pmask) > prefix are kept; of those equal to it, the `rem`
+    // lowest indices: every index <= cut
+    int cut = 0x7FFFFFFF;
+    if (!done) {   // radix select of the rem-th smallest index among keys equal to prefix (digits 9 + 9)
+        uint32_t ipre = 0, imask = 0;
+#pragma unroll 1
+        for (int pass = 0; pass < 2; ++pass) {
+            const int shift = pass == 0 ? 9 : 0;
+            clear_hist();
+            __syncthreads();
+            each_live([&](uint32_t key, int i) {
+                if ((key & pmask) == prefix && ((uint32_t)i & imask) == ipre)
+                    atomicAdd(&hc[(((uint32_t)i >> shift) & 511u) * kCopies], 1u);
+            });
+            __syncthreads();
+            if (wave == 0) pick_digit(sm, kBins, rem, false);
+            __syncthreads();
+            ipre |= sm.sel_bin << shift;
+            imask |= 511u << shift;
+            rem = sm.sel_rem;
+            __syncthreads();
+        }
+        cut = (int)ipre;
+    }
+    if (!whole_bin) {   // the kept keys of bin b0 join the bitmap
+        each_live([&](uint32_t key, int i) {
+            const uint32_t km = key & pmask;
+            if ((key >> 21) == b0 && (km > prefix || (km == prefix && i <= cut)))
+                atomicOr(&sm.bitmap[i >> 5], 1u << (i & 31));
+        });
+    }
+    __syncthreads();
+    {
+        const int W = (nwords + NT - 1) / NT;     // words per thread, in order
+        const int w0 = min(nwords, tid * W), w1 = min(nwords, w0 + W);
+        uint32_t cnt = 0;
+        for (int w = w0; w < w1; ++w) cnt += (uint32_t)__builtin_popcount(sm.bitmap[w]);
+        uint32_t total;
+        uint32_t pos = block_excl_scan(sm, cnt, total);
+        for (int w = w0; w < w1; ++w) {
+            uint32_t bits = sm.bitmap[w];
+            while (bits) {
+                const int b = __builtin_ctz(bits);
+                bits &= bits - 1;
+                if (pos < (uint32_t)k) sm.stage[pos] = 32 * w + b;   // exactly k are kept
+                ++pos;
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < k; i += NT) out[i] = sm.stage[i];
+    for (int b = tid; b < kFusedRowWords; b += NT) zr[b] = 0u;   // histogram and header, for the next call
+}
+
 int topk_parts(int32_t n_q, int64_t ld, int32_t k) {
     // split only when the rows alone cannot fill the chip: about one part per
     // CU of a 256-CU device (one round of workgroups measured faster than two
@@ -558,6 +892,25 @@ hipError_t topk_static_workspace(void **ptr, size_t *bytes) {
     *ptr = g_scratch_ptr[dev];
     *bytes = kTopkStaticBytes;
     return hipSuccess;
+}
+
+hipError_t launch_topk_fused(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k,
+                             int32_t *idx, uint32_t *ws, hipStream_t stream) {
+    const int64_t parts = (ld + kFusedPart - 1) / kFusedPart;
+    dim3 grid((unsigned)n_q, (unsigned)(parts > 0 ? parts : 1));
+    // scores is 16-byte aligned (checked by the API), so rows are when ld % 4 == 0
+    if ((ld & 3) == 0) {
+        hipLaunchKernelGGL(topk_fused_part_kernel<true>, grid, dim3(kFusedPartNT), 0, stream, scores, ld, q_pos, k,
+                           ws);
+        hipLaunchKernelGGL(topk_fused_merge_kernel<true>, dim3((unsigned)n_q), dim3(kFusedMergeNT), 0, stream,
+                           scores, ld, q_pos, k, idx, ws);
+    } else {
+        hipLaunchKernelGGL(topk_fused_part_kernel<false>, grid, dim3(kFusedPartNT), 0, stream, scores, ld, q_pos, k,
+                           ws);
+        hipLaunchKernelGGL(topk_fused_merge_kernel<false>, dim3((unsigned)n_q), dim3(kFusedMergeNT), 0, stream,
+                           scores, ld, q_pos, k, idx, ws);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k, int32_t *idx,

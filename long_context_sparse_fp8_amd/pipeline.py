@@ -1,7 +1,7 @@
 """One pass of the DSA hot path, as a sequence of C-ABI calls.
 
 prefill_step: cache stores -> indexer scores -> top-k -> sparse MLA (prefill)
-decode_step:  cache stores -> indexer scores -> top-k -> sparse MLA (decode)
+decode_step:  cache stores -> indexer scores + top-k (fused) -> sparse MLA (decode)
 
 The caller owns every buffer (`PrefillState` / `DecodeState` hold them so a
 timed loop allocates nothing); each stage is one call into libdsa.so on the
@@ -69,27 +69,43 @@ class DecodeState:
     ws: torch.Tensor               # sparse MLA decode workspace (uint8)
     n_splits: int
     topk_ws: Optional[torch.Tensor] = None   # top-k workspace (uint8), None when rows are not split
+    fused_ws: Optional[torch.Tensor] = None  # workspace of the fused indexer -> top-k (uint8, zeroed once)
 
 
-def alloc_decode(batch, ld, k, h, n_splits=0, device="cuda"):
+def alloc_decode(batch, ld, k, h, n_splits=0, fused=True, device="cuda"):
     """Buffers of one decode step over contexts of up to `ld` tokens.  The score
     rows are padded to a multiple of 64 columns so every row is 256-byte aligned
-    (the top-k then reads them with 16-byte vector loads).  Both workspaces are
-    allocated here, so a step allocates nothing."""
+    (the top-k then reads them with 16-byte vector loads).  Every workspace is
+    allocated here, so a step allocates nothing.  fused (up to 256 queries): the
+    indexer and top-k run as one fused call (its workspace is zeroed here once;
+    every call leaves it ready for the next); otherwise as two calls, the long
+    rows split over several workgroups."""
     need = B.sparse_mla_decode_workspace_size(batch, h, k, n_splits)
     ld = (ld + 63) // 64 * 64
-    tk = B.topk_workspace_size(batch, ld, k)
+    fused = fused and batch <= B.INDEXER_DECODE_MAX_Q
+    tk = 0 if fused else B.topk_workspace_size(batch, ld, k)
     return DecodeState(scores=torch.empty((batch, ld), dtype=torch.float32, device=device),
                        idx=torch.empty((batch, k), dtype=torch.int32, device=device),
                        out=torch.empty((batch, h, B.DV), dtype=torch.bfloat16, device=device),
                        lse=torch.empty((batch, h), dtype=torch.float32, device=device),
                        ws=torch.empty(max(need, 1), dtype=torch.uint8, device=device), n_splits=n_splits,
-                       topk_ws=torch.empty(tk, dtype=torch.uint8, device=device) if tk else None)
+                       topk_ws=torch.empty(tk, dtype=torch.uint8, device=device) if tk else None,
+                       fused_ws=torch.zeros(B.indexer_topk_workspace_size(batch), dtype=torch.uint8, device=device)
+                       if fused else None)
+
+
+def decode_select(ds: DecodeState, caches: PrefillState, iq, iq_scale, w, page_table, q_seq, q_pos, k):
+    """Indexer scores and top-k of a decode step (fused when ds holds the histogram workspace)."""
+    if ds.fused_ws is not None:
+        B.indexer_topk(iq, iq_scale, w, caches.key_cache, caches.key_scale, page_table, q_seq, q_pos, ds.scores, k,
+                       ds.idx, ds.fused_ws)
+    else:
+        B.indexer_scores(iq, iq_scale, w, caches.key_cache, caches.key_scale, page_table, q_seq, q_pos, ds.scores)
+        B.topk(ds.scores, q_pos, k, ds.idx, ws=ds.topk_ws)
 
 
 def decode_step(ds: DecodeState, caches: PrefillState, iq, iq_scale, w, page_table, kv_slot_table, q_seq, q_pos, q,
                 k, sm_scale):
-    B.indexer_scores(iq, iq_scale, w, caches.key_cache, caches.key_scale, page_table, q_seq, q_pos, ds.scores)
-    B.topk(ds.scores, q_pos, k, ds.idx, ws=ds.topk_ws)
+    decode_select(ds, caches, iq, iq_scale, w, page_table, q_seq, q_pos, k)
     B.sparse_mla_decode(q, caches.kv_cache, kv_slot_table, q_seq, ds.idx, sm_scale, ds.out, ds.lse,
                         kv_scale=caches.kv_scale, n_splits=ds.n_splits, ws=ds.ws)

@@ -88,6 +88,35 @@ def test_topk_validation(L):
     assert L.dsa_topk_workspace_size(300, 131072, 2048) == 0
 
 
+def test_indexer_topk_validation(L):
+    """The fused indexer -> top-k call: decode form only, its workspace size,
+    the two calls' shape checks."""
+    per_row = (2048 + 16) * 4 + (262144 // 32 + 2 * 8192) * 4   # zero region + bitmap and candidate list
+    assert per_row == 106560
+    assert L.dsa_indexer_topk_workspace_size(64) == 64 * per_row
+    assert L.dsa_indexer_topk_workspace_size(0) == 0
+    ws = 64 * per_row
+    args = lambda **kw: [kw.get("q", A), A, A, kw.get("w_ld", 64), A, A, 10, A, 4, A, A, kw.get("n_q", 64),
+                         kw.get("h_i", 64), 128, kw.get("scores", A), kw.get("ld", 1000), kw.get("k", 2048),
+                         A, kw.get("ws", A), kw.get("ws_bytes", ws), None]
+    assert L.dsa_indexer_topk(*args(n_q=257)) == 3 and "decode form" in _err(L)
+    assert L.dsa_indexer_topk(*args(h_i=32)) == 3
+    assert L.dsa_indexer_topk(*args(k=0)) == 3
+    assert L.dsa_indexer_topk(*args(k=2049)) == 3
+    assert L.dsa_indexer_topk(*args(ld=262145)) == 3
+    assert L.dsa_indexer_topk(*args(ld=0)) == 2
+    assert L.dsa_indexer_topk(*args(w_ld=7)) == 2
+    assert L.dsa_indexer_topk(*args(n_q=-1)) == 2
+    assert L.dsa_indexer_topk(*args(q=None)) == 1
+    assert L.dsa_indexer_topk(*args(scores=MIS)) == 4
+    assert L.dsa_indexer_topk(*args(ws_bytes=ws - 1)) == 5
+    assert L.dsa_indexer_topk(*args(ws=None)) == 1
+    assert L.dsa_indexer_topk(*args(ws=MIS)) == 4
+    # n_q == 0 is a no-op, even with NULL pointers
+    assert L.dsa_indexer_topk(None, None, None, 64, None, None, 10, None, 4, None, None, 0, 64, 128, None, 1000,
+                              2048, None, None, 0, None) == 0
+
+
 def test_mla_validation(L):
     f = ctypes.c_float(1 / 24)
     args = lambda **kw: [kw.get("q", A), A, kw.get("kvs", A), kw.get("dt", 0), kw.get("n_slots", 100), A,

@@ -14,6 +14,8 @@ the last bits):
 Sparse-MLA outputs are compared with the oracle evaluated on the GPU's own
 indices: max-abs relative error <= 2e-2 (bf16 KV) and 5e-2 (FP8 KV).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -802,3 +804,201 @@ def test_decode_graph_replay_matches_eager():
             assert torch.equal(a, b), r
         for a, b in zip(ref, (other.idx, other.out, other.lse)):
             assert torch.equal(a, b), r
+
+
+# ------------------------------------------------------------------ fused indexer -> top-k (decode form)
+def _decode_keys(batch, lo, hi, m):
+    """Seeded decode inputs (queries at the last m positions) and the indexer key cache."""
+    c = CONFIGS["C4"]
+    inp = synth.make_decode(c, batch=batch, ctx_lo=lo, ctx_hi=hi, queries_per_seq=m, device=DEV)
+    key_cache = torch.zeros((inp.n_pages, 64, c.d_i), dtype=torch.uint8, device=DEV)
+    key_scale = torch.zeros((inp.n_pages, 64), dtype=torch.float32, device=DEV)
+    dsa.indexer_cache_store(inp.ik, inp.ik_scale, inp.ik_slot, key_cache, key_scale)
+    return inp, key_cache, key_scale
+
+
+def _two_calls(inp, key_cache, key_scale, table, ld, k):
+    n_q = inp.iq.shape[0]
+    sc = torch.full((n_q, ld), -7.0, device=DEV)
+    idx = torch.full((n_q, k), -9, dtype=torch.int32, device=DEV)
+    dsa.indexer_scores(inp.iq, inp.iq_scale, inp.w, key_cache, key_scale, table, inp.q_seq, inp.q_pos, sc)
+    need = dsa.topk_workspace_size(n_q, ld, k)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
+    dsa.topk(sc, inp.q_pos, k, idx, ws=ws if need else None)
+    return sc, idx
+
+
+FUSED_ROW_BYTES, FUSED_ZERO_BYTES = 106560, 8256
+
+
+def _fused_zero_regions_clear(ws):
+    """Every row block's leading region (histogram and counters) is zero again."""
+    rows = ws.numel() // FUSED_ROW_BYTES
+    return int(ws[: rows * FUSED_ROW_BYTES].view(rows, FUSED_ROW_BYTES)[:, :FUSED_ZERO_BYTES].count_nonzero()) == 0
+
+
+def _fused(inp, key_cache, key_scale, table, ld, k, ws):
+    n_q = inp.iq.shape[0]
+    sc = torch.full((n_q, ld), -7.0, device=DEV)
+    idx = torch.full((n_q, k), -9, dtype=torch.int32, device=DEV)
+    dsa.indexer_topk(inp.iq, inp.iq_scale, inp.w, key_cache, key_scale, table, inp.q_seq, inp.q_pos, sc, k, idx, ws)
+    return sc, idx
+
+
+@pytest.mark.parametrize("batch,lo,hi,m,k,variant", [
+    (8, 2000, 9000, 1, 2048, "plain"),          # rows held in registers
+    (4, 33000, 70000, 1, 2048, "plain"),        # rows longer than 32K: streamed
+    (6, 1500, 20000, 2, 2048, "plain"),         # query pairs of one sequence share the scan
+    (8, 100, 3000, 1, 2048, "plain"),           # contexts below k: every candidate kept
+    (5, 5000, 9000, 1, 1, "plain"),
+    (5, 5000, 9001, 1, 64, "odd_ld"),           # rows not 16-byte aligned
+    (4, 9000, 40000, 1, 2048, "short_table"),   # pages past the table: NaN scores
+    (3, 9000, 12000, 1, 2048, "ties"),          # all scores equal: the threshold bin overflows the list
+    (2, 40000, 50000, 1, 512, "ties"),          # ... in streamed rows
+    (2, 120000, 131072, 1, 2048, "plain"),      # the longest decode contexts: 4 parts per row
+    (2, 65536, 65536, 1, 2048, "plain"),        # rows of exactly 2 parts
+])
+def test_indexer_topk_fused_matches_two_calls(batch, lo, hi, m, k, variant):
+    """dsa_indexer_topk writes the same scores and indices, bit for bit, as
+    dsa_indexer_scores followed by dsa_topk; the indices equal the oracle's top-k
+    of those scores; the workspace's histogram and counters are zero again after
+    every call, so a second call (fewer queries, same workspace) is exact too."""
+    say(f"[fused] B={batch} ctx=[{lo},{hi}] queries/seq={m} k={k} {variant}")
+    inp, key_cache, key_scale = _decode_keys(batch, lo, hi, m)
+    if variant == "ties":
+        inp = dataclasses.replace(inp, w=torch.zeros_like(inp.w))
+    ld = int(inp.lens.max())
+    if variant == "odd_ld":
+        ld |= 1
+    table = inp.page_table
+    if variant == "short_table":
+        table = table[:, :100].contiguous()
+    n_q = inp.iq.shape[0]
+    ws = torch.zeros(dsa.indexer_topk_workspace_size(n_q), dtype=torch.uint8, device=DEV)
+    sa, ia = _two_calls(inp, key_cache, key_scale, table, ld, k)
+    sb, ib = _fused(inp, key_cache, key_scale, table, ld, k, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sa.view(torch.int32), sb.view(torch.int32))
+    assert torch.equal(ia, ib)
+    assert _fused_zero_regions_clear(ws)
+    g = sb.cpu().numpy()
+    pos = inp.q_pos.cpu().numpy()
+    if variant == "short_table":
+        assert np.isnan(g[0, 6400:pos[0] + 1]).all()
+    else:
+        np.testing.assert_array_equal(ib.cpu().numpy(), oracle.topk(g, pos, k))
+    # a second call on the same (zero again) workspace, fewer queries
+    half = dataclasses.replace(inp, iq=inp.iq[: n_q // 2 + 1], iq_scale=inp.iq_scale[: n_q // 2 + 1],
+                               w=inp.w[: n_q // 2 + 1], q_seq=inp.q_seq[: n_q // 2 + 1],
+                               q_pos=inp.q_pos[: n_q // 2 + 1])
+    sc2, ic2 = _fused(half, key_cache, key_scale, table, ld, k, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ic2, ia[: n_q // 2 + 1])
+    assert torch.equal(sc2.view(torch.int32), sa[: n_q // 2 + 1].view(torch.int32))
+    assert _fused_zero_regions_clear(ws)
+
+
+def test_indexer_topk_fused_graph_replay():
+    """The fused call captured in a HIP graph: every replay (eager fused calls on
+    the same workspace in between) gives the eager indices, and the workspace's
+    histogram and counters are zero after each."""
+    say("[fused] graph replay")
+    inp, key_cache, key_scale = _decode_keys(6, 3000, 40000, 1)
+    ld, k, n_q = int(inp.lens.max()), 2048, 6
+    ws = torch.zeros(dsa.indexer_topk_workspace_size(n_q), dtype=torch.uint8, device=DEV)
+    sc = torch.zeros((n_q, ld), device=DEV)
+    idx = torch.zeros((n_q, k), dtype=torch.int32, device=DEV)
+    call = lambda: dsa.indexer_topk(inp.iq, inp.iq_scale, inp.w, key_cache, key_scale, inp.page_table, inp.q_seq,
+                                    inp.q_pos, sc, k, idx, ws)
+    call()
+    torch.cuda.synchronize()
+    ref = idx.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(3):
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref), r
+        assert _fused_zero_regions_clear(ws), r
+        call()                          # eager work on the same workspace between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref), r
+
+
+def _crafted_rows(values):
+    """Indexer inputs whose scores are exactly `values` [n_q, n]: one weighted head,
+    q = e_0 (FP8 1.0), key s = values[., s] in dimension 0 (FP8), unit scales;
+    query r is the last token of sequence r (identity page tables)."""
+    n_q, n = values.shape
+    pages = (n + 63) // 64
+    codes = torch.from_numpy(values.astype(np.float32)).to(torch.float8_e4m3fn)
+    assert np.array_equal(codes.float().numpy(), values.astype(np.float32)), "not exactly representable"
+    ik = torch.zeros((n_q * pages * 64, 128), dtype=torch.uint8)
+    for r in range(n_q):
+        ik[r * pages * 64: r * pages * 64 + n, 0] = codes[r].view(torch.uint8)
+    key_cache = torch.zeros((n_q * pages, 64, 128), dtype=torch.uint8, device=DEV)
+    key_scale = torch.zeros((n_q * pages, 64), dtype=torch.float32, device=DEV)
+    dsa.indexer_cache_store(ik.to(DEV), torch.ones(ik.shape[0], device=DEV),
+                            torch.arange(ik.shape[0], dtype=torch.int64, device=DEV), key_cache, key_scale)
+    iq = torch.zeros((n_q, 64, 128), dtype=torch.uint8)
+    iq[:, 0, 0] = 0x38                                          # E4M3 1.0
+    w = torch.zeros((n_q, 64))
+    w[:, 0] = 1.0
+    table = torch.arange(n_q * pages, dtype=torch.int32).reshape(n_q, pages)
+    inp = dataclasses.make_dataclass("Crafted", ["iq", "iq_scale", "w", "q_seq", "q_pos", "page_table"])(
+        iq.to(DEV), torch.ones(n_q, device=DEV), w.to(DEV), torch.arange(n_q, dtype=torch.int32, device=DEV),
+        torch.full((n_q,), n - 1, dtype=torch.int32, device=DEV), table.to(DEV))
+    return inp, key_cache, key_scale
+
+
+@pytest.mark.parametrize("pattern", ["wave_overflow", "spread_ties", "big_bin", "whole_bin", "last_part_one_key"])
+def test_indexer_topk_fused_crafted_scores(pattern):
+    """Score rows built to reach each path of the fused selection (parts of 32768
+    scores, 16 waves of a part each owning 256 of every 4096): the threshold bin's
+    keys crowded into one wave's slots (its list overflows), spread ties (the
+    list path), a bin larger than the list (the whole row re-read), a bin taken
+    whole, and a last part of one score.  Indices equal the two calls' and the
+    oracle's, bit for bit."""
+    say(f"[fused] crafted scores: {pattern}")
+    rng = np.random.default_rng(sum(map(ord, pattern)))
+    n, k = (40000, 1000) if pattern != "last_part_one_key" else (65537, 2048)
+    vals = np.full((2, n), 0.5)
+    for r in range(2):
+        if pattern == "wave_overflow":          # wave 0's slots of every chunk of part 0
+            pos = (np.arange(8)[:, None] * 4096 + np.arange(256)[None, :]).ravel()
+            vals[r, pos] = rng.choice([2.0, 2.25], size=pos.size)
+        elif pattern == "spread_ties":
+            pos = rng.choice(n, 5000, replace=False)
+            vals[r, pos] = rng.choice([2.0, 2.25], size=pos.size)
+        elif pattern == "big_bin":
+            pos = rng.choice(n, 10000, replace=False)
+            vals[r, pos] = rng.choice([2.0, 2.25], size=pos.size)
+        elif pattern == "whole_bin":
+            perm = rng.permutation(n)
+            vals[r, perm[:k]] = 4.0
+            vals[r, perm[k:k + 3000]] = np.where(rng.random(3000) < 0.5, 0.75, 1.0)
+        else:                                   # the row's last score is the only one of part 2
+            codes = torch.from_numpy(rng.integers(0x20, 0x70, size=n).astype(np.uint8))
+            vals[r] = codes.view(torch.float8_e4m3fn).double().numpy()
+            vals[r, -1] = 448.0
+    inp, key_cache, key_scale = _crafted_rows(vals)
+    ws = torch.zeros(dsa.indexer_topk_workspace_size(2), dtype=torch.uint8, device=DEV)
+    sa, ia = _two_calls(inp, key_cache, key_scale, inp.page_table, n, k)
+    sb, ib = _fused(inp, key_cache, key_scale, inp.page_table, n, k, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sb.cpu().numpy(), vals.astype(np.float32))
+    assert torch.equal(sa.view(torch.int32), sb.view(torch.int32))
+    want = oracle.topk(vals.astype(np.float32), np.full(2, n - 1), k)
+    np.testing.assert_array_equal(ib.cpu().numpy(), want)
+    np.testing.assert_array_equal(ia.cpu().numpy(), want)
+    assert _fused_zero_regions_clear(ws)
+    if pattern == "last_part_one_key":
+        assert (ib.cpu().numpy() == n - 1).any(axis=1).all()
