@@ -260,9 +260,10 @@ def run_decode_step(cfg, inp, caches, newest, ds, timer=None):
     if e: e.record()
 
 
-def decode_kernels(db, stages):
+def decode_kernels(db, stages, mla_traffic_key="sparse_mla_decode"):
     """Achieved HBM rate of each decode stage from its algorithmic bytes (a fused
-    indexer -> top-k stage carries the bytes of both)."""
+    indexer -> top-k stage carries the bytes of both), with the recorded HBM
+    traffic of the 64-query launches where it applies."""
     parts = ([("indexer_topk", db["indexer_bytes"] + db["topk_bytes"], "indexer_topk")] if "indexer_topk" in stages
              else [("indexer", db["indexer_bytes"], "indexer"), ("topk", db["topk_bytes"], "topk")])
     parts.append(("sparse_mla_decode", db["mla_bytes"], "mla"))
@@ -271,8 +272,11 @@ def decode_kernels(db, stages):
         gbs = nbytes / (stages[st] * 1e-3) / 1e9
         out[name] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s", "us": stages[st] * 1e3,
                      "frac": gbs / PEAK_HBM}
-    if "indexer" in out:
-        out["indexer"]["traffic"] = recorded_traffic("indexer_decode")
+    # HBM bytes per launch from the recorded counter runs (null when not recorded for these sources)
+    if "indexer_topk" in out:
+        parts = [recorded_traffic(n) for n in ("indexer_decode", "topk_fused_part", "topk_fused_merge")]
+        out["indexer_topk"]["traffic"] = None if None in parts else sum(parts)
+    out["sparse_mla_decode"]["traffic"] = recorded_traffic(mla_traffic_key) if mla_traffic_key else None
     return out
 
 
@@ -637,7 +641,7 @@ def main():
         ds2 = P.alloc_decode(2 * dcfg.decode_batch, int(dinp.lens.max()), dcfg.k, dcfg.h, device=dev)
         dwall2, dst2 = time_decode(args, dcfg, dinp2, caches, newest2, ds2)
         db2 = decode_bytes(dinp2, dcfg.k, dcfg.h)
-        dk2 = decode_kernels(db2, dst2)
+        dk2 = decode_kernels(db2, dst2, mla_traffic_key=None)   # 128 queries: other launch shapes
         result["decode_mtp2"] = {
             "workload": "the decode step above with 2 query tokens per sequence (positions N-2, N-1): 128 queries",
             "us_per_step": dwall2 * 1e6, "tokens_per_s": 2 * dcfg.decode_batch / dwall2,
@@ -654,7 +658,8 @@ def main():
             "us_per_step": dwall8 * 1e6, "tokens_per_s": dcfg.decode_batch / dwall8,
             "stages_us": {k2: v * 1e3 for k2, v in dst8.items()},
             "kernels": {"sparse_mla_decode": {"bound": "hbm", "achieved": mla8, "peak": PEAK_HBM, "unit": "GB/s",
-                                              "us": dst8["mla"] * 1e3, "frac": mla8 / PEAK_HBM}}}
+                                              "us": dst8["mla"] * 1e3, "frac": mla8 / PEAK_HBM,
+                                              "traffic": recorded_traffic("sparse_mla_decode_fp8")}}}
         log(f"[bench] decode, FP8 latent cache: {dwall8 * 1e6:.1f} us/step; stages us "
             f"{result['decode_fp8_kv']['stages_us']}")
         del caches, dinp, ds, kv_slot
