@@ -8,27 +8,28 @@
 //
 // One workgroup per row: 512 threads when many rows of at most 32K scores are
 // selected at once (two workgroups share a CU, so one row's barriers and loads
-// overlap the other's work), else 1024.  Every score is touched by only three
+// overlap the other's work), else 1024.  Every score is touched by only two
 // cheap sweeps:
 //   1. an 11-bit histogram of the top key bits (sign, exponent, two mantissa
 //      bits) in LDS, NT / 128 lane-interleaved copies; a block scan of the 2048
 //      bins from the top finds the bin holding the k-th largest key;
-//   2. the keys of that bin (a few percent of the row) are collected into an
-//      LDS candidate list, and the radix select finishes on the list alone
-//      (8-, 8- and 5-bit digits; it stops early once a bin is taken whole).
-//      Ties at the threshold key T are resolved by a second radix select over
-//      the candidates' indices: the `need` lowest indices equal to T are kept,
-//      i.e. every index up to a cut.  If the bin overflows the list (a row of
-//      mostly equal scores) the same passes run over the whole row instead;
-//   3. every kept score (key > T, or key == T at an index up to the cut) sets
-//      its bit in an LDS bitmap of the row; a block scan of the bitmap words'
-//      popcounts then writes the kept indices in ascending order.
+//   2. every key above that bin sets its bit in an LDS bitmap of the kept
+//      indices, and the bin's own keys (a few percent of the row) go to
+//      per-wave LDS candidate lists (ballot and lane count, no atomics).  The
+//      radix select finishes on the lists alone (8-, 8- and 5-bit digits; it
+//      stops early once a bin is taken whole).  Ties at the threshold key T are
+//      resolved by a second radix select over the candidates' indices: the
+//      `need` lowest indices equal to T are kept, i.e. every index up to a cut.
+//      The kept candidates (key > T, or key == T at an index up to the cut)
+//      join the bitmap, and a block scan of the bitmap words' popcounts writes
+//      the kept indices in ascending order.  If a wave's list overflows (a row
+//      of mostly equal scores) the same passes run over the whole row instead.
 // Scores become order-preserving uint32 keys.  The row is cut into chunks of
 // 4 NT scores (NT threads); in chunk c thread i owns the four consecutive
 // scores starting at c * 4 NT + 4 i, so every wave-wide load is one contiguous
 // 1 KB run.  Rows of at most 4 NT C scores are read once and kept in registers
-// (every prefill row here); longer rows are streamed chunk by chunk for each
-// sweep (they are few: one per decode sequence, and the re-reads hit L2).
+// (every row of a 32K prefill); longer rows are streamed for each sweep,
+// kStreamAhead chunks in flight per thread.
 // Everything is integer, so the selection is exact for the given scores.
 //
 // Few long rows (decode: one row of up to 128K scores per sequence) would leave
@@ -51,6 +52,7 @@ namespace dsa {
 constexpr int kBins0 = 2048;                    // first digit: key bits 31..21
 constexpr int kBins = 512;                      // later digits (<= 9 bits)
 constexpr int kCopies = 4;                      // lane-interleaved copies of the later histograms
+constexpr int kStreamAhead = 8;                 // chunks in flight per thread when a row is streamed
 
 // Workgroup shape: NT threads (1024, or 512 for rows of at most 32K scores,
 // two workgroups per CU), chunks of 4 NT scores; C > 0 chunks per row in
@@ -83,7 +85,8 @@ struct TopkSmem {
     uint32_t bitmap[S::kWords];
     int32_t stage[kTopkMaxK];
     uint32_t wsum[S::kWaves];
-    uint32_t sel_bin, sel_rem, sel_done, n_cand;
+    uint32_t wcnt[S::kWaves];                   // per-wave candidate list lengths
+    uint32_t sel_bin, sel_rem, sel_done;
 };
 
 // Block-wide exclusive scan (all NT threads call it); returns the sum over
@@ -272,13 +275,21 @@ __global__ __launch_bounds__(NT, 1024 / NT) void topk_kernel(const float *__rest
                 }
             }
         } else {
-            for (int c = 0; c < nc; ++c) {
-                uint32_t key[4];
-                load_chunk<NT, VEC>(row, n, c, key);
+            // kStreamAhead chunks per step, all loads issued before the first is used
+            // (the chunk index is clamped, so the loads need no branch)
+            for (int c0 = 0; c0 < nc; c0 += kStreamAhead) {
+                uint32_t key[kStreamAhead][4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = c * kChunk + 4 * tid + e;
-                    if (i < n) fn(key[e], i);
+                for (int u = 0; u < kStreamAhead; ++u) load_chunk<NT, VEC>(row, n, min(c0 + u, nc - 1), key[u]);
+#pragma unroll
+                for (int u = 0; u < kStreamAhead; ++u) {
+                    if (c0 + u < nc) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = (c0 + u) * kChunk + 4 * tid + e;
+                            if (i < n) fn(key[u][e], i);
+                        }
+                    }
                 }
             }
         }
@@ -343,33 +354,48 @@ __global__ __launch_bounds__(NT, 1024 / NT) void topk_kernel(const float *__rest
         else each_key(Unchecked{}, fn);
     };
 
-    // ---- sweep 2: collect the threshold bin's keys (unless it is taken whole)
-    bool use_list = false;
-    uint32_t n_cand = 0;
-    if (!done) {
-        uint32_t mine = 0;
-        each_row([&](uint32_t key, int) { mine += (key >> 21) == b0 ? 1u : 0u; });
-        uint32_t total;
-        uint32_t pos = block_excl_scan(sm, mine, total);   // also orders hist0 reads before the list writes
-        n_cand = total;
-        use_list = total <= (uint32_t)S::kCandCap;
-        if (use_list) {
-            each_row([&](uint32_t key, int i) {
-                if ((key >> 21) == b0) {
-                    sm.cand.key[pos] = key;
-                    sm.cand.idx[pos] = i;
-                    ++pos;
+    // ---- sweep 2: every key above the threshold bin (and the bin itself when it
+    // is taken whole) sets its bit in the bitmap of kept indices; the bin's keys
+    // go to per-wave LDS lists (ballot and lane count, no atomics).  A wave list
+    // that overflows (a row of mostly equal scores) makes the select finish over
+    // the whole row instead.
+    const bool whole_bin = done;
+    constexpr int R = S::kCandCap / S::kWaves;     // per-wave list capacity
+    const int nwords = (n + 31) >> 5;
+    clear(sm.bitmap, (nwords + 3) & ~3);
+    __syncthreads();                               // (the first-digit reads of hist0, which the lists alias, are done)
+    {
+        uint32_t wfill = 0;                        // this wave's list length (uniform)
+        each_row([&](uint32_t key, int i) {
+            const uint32_t bin = key >> 21;
+            if (bin > b0 || (whole_bin && bin == b0)) atomicOr(&sm.bitmap[i >> 5], 1u << (i & 31));
+            if (!whole_bin) {
+                const bool me = bin == b0;
+                const uint64_t m = __ballot(me);
+                if (m != 0ull) {
+                    const uint32_t slot = wfill + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (me && slot < (uint32_t)R) {
+                        sm.cand.key[wave * R + slot] = key;
+                        sm.cand.idx[wave * R + slot] = i;
+                    }
+                    wfill += (uint32_t)__popcll(m);
                 }
-            });
-        }
-        __syncthreads();
+            }
+        });
+        if (lane == 0) sm.wcnt[wave] = wfill;
     }
-    // fn(key, index) over the elements still in play: the candidate list, or (a
-    // row of mostly equal scores that overflows the list) the whole row, re-read
-    // from memory so that the register copy stays out of the pass loops
+    __syncthreads();
+    bool use_list = !whole_bin;
+#pragma unroll
+    for (int w = 0; w < S::kWaves; ++w) use_list = use_list && sm.wcnt[w] <= (uint32_t)R;
+    const uint32_t my_cnt = sm.wcnt[wave];
+    // fn(key, index) over the elements still in play: each wave's own candidate
+    // list, or (a list overflowed) the whole row, re-read from memory so that the
+    // register copy stays out of the pass loops
     auto each_live = [&](auto fn) {
         if (use_list) {
-            for (int j = tid; j < (int)n_cand; j += NT) fn(sm.cand.key[j], sm.cand.idx[j]);
+            for (int j = lane; j < (int)my_cnt; j += kWave) fn(sm.cand.key[wave * R + j], sm.cand.idx[wave * R + j]);
         } else {
             for (int c = 0; c < nc; ++c) {
                 uint32_t key[4];
@@ -433,14 +459,16 @@ __global__ __launch_bounds__(NT, 1024 / NT) void topk_kernel(const float *__rest
         cut = (int)ipre;
     }
 
-    // ---- sweep 3: bitmap of the kept indices, then ordered output
-    const int nwords = (n + 31) >> 5;
-    clear(sm.bitmap, (nwords + 3) & ~3);
-    __syncthreads();
-    each_row([&](uint32_t key, int i) {
-        const uint32_t km = key & pmask;
-        if (km > prefix || (km == prefix && i <= cut)) atomicOr(&sm.bitmap[i >> 5], 1u << (i & 31));
-    });
+    // ---- the threshold bin's kept keys (key > T, or key == T at an index up to
+    // the cut) join the bitmap (a bin taken whole is there already); then the
+    // ordered output
+    if (!whole_bin) {
+        each_live([&](uint32_t key, int i) {
+            const uint32_t km = key & pmask;
+            if ((key >> 21) == b0 && (km > prefix || (km == prefix && i <= cut)))
+                atomicOr(&sm.bitmap[i >> 5], 1u << (i & 31));
+        });
+    }
     __syncthreads();
     {
         const int W = (nwords + NT - 1) / NT;   // words per thread, in order
