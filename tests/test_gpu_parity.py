@@ -855,8 +855,10 @@ def _fused(inp, key_cache, key_scale, table, ld, k, ws):
     (4, 9000, 40000, 1, 2048, "short_table"),   # pages past the table: NaN scores
     (3, 9000, 12000, 1, 2048, "ties"),          # all scores equal: the threshold bin overflows the list
     (2, 40000, 50000, 1, 512, "ties"),          # ... in streamed rows
-    (2, 120000, 131072, 1, 2048, "plain"),      # the longest decode contexts: 4 parts per row
-    (2, 65536, 65536, 1, 2048, "plain"),        # rows of exactly 2 parts
+    (2, 120000, 131072, 1, 2048, "plain"),      # the longest decode contexts: 8 parts per row
+    (2, 65536, 65536, 1, 2048, "plain"),        # rows of exactly 4 parts
+    (2, 262144, 262144, 1, 2048, "plain"),      # the longest row accepted (16 parts)
+    (128, 1500, 9000, 2, 2048, "plain"),        # 256 queries: the most the fused call takes
 ])
 def test_indexer_topk_fused_matches_two_calls(batch, lo, hi, m, k, variant):
     """dsa_indexer_topk writes the same scores and indices, bit for bit, as
