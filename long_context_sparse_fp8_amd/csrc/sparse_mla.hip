@@ -21,9 +21,13 @@
 //   * the copies of tile j + 1 are spread between the MFMAs of tile j, one
 //     every few MFMAs, so their latency is hidden behind the tile's work;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 gathered rows from LDS,
-//     B = the wave's 32 query heads held in VGPRs), in two 32-row halves, each
-//     followed by its softmax (a wave's VALU work does not overlap its own
-//     MFMAs here, so spreading the softmax between them measured slower);
+//     B = the wave's 32 query heads held in VGPRs), in two 32-row halves with
+//     an accumulator each.  The softmax of half 0 is spread over the MFMAs of
+//     half 1 and that of half 1 over the O^T MFMAs of rows 0..31, a few VALU
+//     instructions per MFMA in a three-stage software pipeline (a wave issues
+//     independent VALU work while its own MFMA executes, but in order, so no
+//     instruction may wait on another of the same slot).  FP8 rows keep each
+//     half's softmax between the MFMAs;
 //   * softmax per head (= per lane column) in the exp2 domain against a fixed
 //     reference: the head's maximum over the first 32 rows.  Probabilities of
 //     later rows may exceed 1 by up to 2^64 before the reference must move; that
@@ -427,36 +431,100 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                 if (partial) body(std::true_type{});
                 else body(std::false_type{});
             };
-            uint4 kr[kLookK<FP8>];
-            bf16x4 vlo[kLookV<FP8>], vhi[kLookV<FP8>];
+            // The MFMA stream of one tile.  SERIAL (FP8 rows): each half's softmax
+            // runs between the MFMAs of S^T and O^T.  bf16 rows: the softmax is spread
+            // over the following MFMAs, about one element per MFMA (an exp2 and five
+            // other VALU instructions, which the wave issues while its MFMA executes):
+            // half 0's under the S^T MFMAs of half 1 (a second accumulator), half 1's
+            // under the O^T MFMAs of rows 0..31, which only need half 0's
+            // probabilities.  Rows past the selection (last tile only) hold copies of
+            // the first selected row, so they change no maximum; their probabilities
+            // are set to zero.
+            auto run = [&](auto serial_c) {
+                constexpr bool kSerial = decltype(serial_c)::value;
+                uint4 kr[kLookK<FP8>];
+                bf16x4 vlo[kLookV<FP8>], vhi[kLookV<FP8>];
+                f32x16 s1;
+                // Softmax of one half, software-pipelined over 18 MFMA slots so that no
+                // instruction in a slot waits for another of the same slot: slot t forms
+                // the logit of element t, exponentiates element t - 1 and masks, sums
+                // and packs element t - 2 (element e: row rl of lanes 0..31, rl + 4 of
+                // lanes 32..63; a row past the selection iff rl >= lim).
+                float xs[3], pes[3], pprev = 0.0f;
+                bool keep[3];
+                auto sm_slot = [&](auto hfc, auto tc, const f32x16 &sv) {
+                    constexpr int hf = decltype(hfc)::value, t = decltype(tc)::value;
+                    if constexpr (t >= 2 && t < 18) {
+                        constexpr int e = t - 2;
+                        const float p = keep[e % 3] ? pes[e % 3] : 0.0f;
+                        psum += p;
+                        asm volatile("" : "+v"(psum));           // summed here, in row order
+                        if constexpr (e & 1) {
+                            const bf16x2 pk = {(__bf16)pprev, (__bf16)p};
+                            pw[2 * hf + (e >> 3)][(e & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+                        } else {
+                            pprev = p;
+                        }
+                    }
+                    if constexpr (t >= 1 && t < 17) {
+                        constexpr int e = t - 1;
+                        pes[e % 3] = __builtin_amdgcn_exp2f(xs[e % 3]);
+                        keep[e % 3] = 32 * hf + 8 * (e >> 2) + (e & 3) < lim;
+                    }
+                    if constexpr (t < 16) {
+                        const float v = sv[t];
+                        rmax = fmaxf(rmax, v);
+                        xs[t % 3] = fmaf(v, c2, -m_ref);
+                    }
+                };
 #pragma unroll
-            for (int f = 0; f < kLookK<FP8>; ++f) kr[f] = kload(f);
-            static_for<kQK>([&](auto fc) {
-                constexpr int f = decltype(fc)::value;
-                constexpr int ks = f % kKSteps;
-                if constexpr (f == kKSteps) softmax_half(0);
-                const uint4 kc = kr[f % kLookK<FP8>];
-                if constexpr (f + kLookK<FP8> < kQK) kr[f % kLookK<FP8>] = kload(f + kLookK<FP8>);
-                else if constexpr (f + kLookK<FP8> - kQK < kLookV<FP8>)
-                    vload(f + kLookK<FP8> - kQK, vlo[f + kLookK<FP8> - kQK], vhi[f + kLookK<FP8> - kQK]);
-                s = mfma32_bf16(__builtin_bit_cast(bf16x8, kc), qf[ks], ks == 0 ? f32x16{} : s);
-                if constexpr (f % kCopyEvery == 0 && f / kCopyEvery < kCopies)
-                    copy_one(std::integral_constant<int, f / kCopyEvery>{}, src, nxt);
-                __builtin_amdgcn_sched_barrier(0);
-            });
-            softmax_half(1);
-            static_for<kPV>([&](auto fc) {
-                constexpr int f = decltype(fc)::value;
-                if constexpr ((f + kQK) % kCopyEvery == 0 && (f + kQK) / kCopyEvery < kCopies)
-                    copy_one(std::integral_constant<int, (f + kQK) / kCopyEvery>{}, src, nxt);
-                const bf16x4 lo = vlo[f % kLookV<FP8>], hi = vhi[f % kLookV<FP8>];
-                if constexpr (f + kLookV<FP8> < kPV) vload(f + kLookV<FP8>, vlo[f % kLookV<FP8>], vhi[f % kLookV<FP8>]);
-                const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                const uint4 bw = make_uint4(pw[f >> 4][0], pw[f >> 4][1], pw[f >> 4][2], pw[f >> 4][3]);
-                if constexpr (f == 0) asm volatile("s_nop 4");   // P^T was just written by VALU code
-                mfma32_bf16_acc(o[f & 15], a, __builtin_bit_cast(bf16x8, bw));
-                __builtin_amdgcn_sched_barrier(0);
-            });
+                for (int f = 0; f < kLookK<FP8>; ++f) kr[f] = kload(f);
+                static_for<kQK>([&](auto fc) {
+                    constexpr int f = decltype(fc)::value;
+                    constexpr int ks = f % kKSteps;
+                    if constexpr (f == kKSteps) {
+                        if constexpr (kSerial) {
+                            softmax_half(0);
+                        } else if (first_attempt && j == 0) {   // reference of every head: max over rows 0..31
+                            float mx = -INFINITY;
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i] * c2);
+                            m_ref = fmaxf(mx, swap_halves(mx));
+                        }
+                    }
+                    const uint4 kc = kr[f % kLookK<FP8>];
+                    if constexpr (f + kLookK<FP8> < kQK) kr[f % kLookK<FP8>] = kload(f + kLookK<FP8>);
+                    else if constexpr (f + kLookK<FP8> - kQK < kLookV<FP8>)
+                        vload(f + kLookK<FP8> - kQK, vlo[f + kLookK<FP8> - kQK], vhi[f + kLookK<FP8> - kQK]);
+                    if constexpr (kSerial || f < kKSteps)
+                        s = mfma32_bf16(__builtin_bit_cast(bf16x8, kc), qf[ks], ks == 0 ? f32x16{} : s);
+                    else
+                        s1 = mfma32_bf16(__builtin_bit_cast(bf16x8, kc), qf[ks], ks == 0 ? f32x16{} : s1);
+                    if constexpr (f % kCopyEvery == 0 && f / kCopyEvery < kCopies)
+                        copy_one(std::integral_constant<int, f / kCopyEvery>{}, src, nxt);
+                    if constexpr (!kSerial && f >= kKSteps + 2 && f < kKSteps + 20)
+                        sm_slot(std::integral_constant<int, 0>{}, std::integral_constant<int, f - kKSteps - 2>{}, s);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                if constexpr (kSerial) softmax_half(1);
+                static_for<kPV>([&](auto fc) {
+                    constexpr int f = decltype(fc)::value;
+                    if constexpr ((f + kQK) % kCopyEvery == 0 && (f + kQK) / kCopyEvery < kCopies)
+                        copy_one(std::integral_constant<int, (f + kQK) / kCopyEvery>{}, src, nxt);
+                    const bf16x4 lo = vlo[f % kLookV<FP8>], hi = vhi[f % kLookV<FP8>];
+                    if constexpr (f + kLookV<FP8> < kPV) vload(f + kLookV<FP8>, vlo[f % kLookV<FP8>], vhi[f % kLookV<FP8>]);
+                    const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const uint4 bw = make_uint4(pw[f >> 4][0], pw[f >> 4][1], pw[f >> 4][2], pw[f >> 4][3]);
+                    // wait states: P^T was just written by VALU code (serial: before the
+                    // first O^T MFMA; overlapped: half 1's before the first MFMA of rows 32..63)
+                    if constexpr (kSerial ? f == 0 : f == kPV / 2) asm volatile("s_nop 4");
+                    mfma32_bf16_acc(o[f & 15], a, __builtin_bit_cast(bf16x8, bw));
+                    if constexpr (!kSerial && f >= 2 && f < 20)
+                        sm_slot(std::integral_constant<int, 1>{}, std::integral_constant<int, f - 2>{}, s1);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
+            run(std::integral_constant<bool, FP8>{});
             float tmax = FP8 ? rmax : rmax * c2;          // c2 > 0: the max of the log2 logits
             tmax = fmaxf(tmax, swap_halves(tmax));
             m_seen = fmaxf(m_seen, tmax);
