@@ -878,13 +878,18 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_hg_kernel(
             VFrag vr[kLookV];
 #pragma unroll
             for (int f = 0; f < kLookK; ++f) kr[f] = kload(f);
+            // FP8: each K fragment is expanded one k-step ahead, under the MFMAs of
+            // the step before, so that no MFMA waits on its own conversion
+            bf16x8 a_next;
+            if constexpr (FP8) a_next = kfrag(kr[0]);
             static_for<kK32>([&](auto kc) {
                 constexpr int ks = decltype(kc)::value;
-                const bf16x8 a = kfrag(kr[ks % kLookK]);
+                const bf16x8 a = FP8 ? a_next : kfrag(kr[ks % kLookK]);
                 if constexpr (ks + kLookK < kK32) kr[ks % kLookK] = kload(ks + kLookK);
                 else vr[ks + kLookK - kK32] = vload(ks + kLookK - kK32);
                 s[0] = mfma16_bf16(a, qf[0][ks], s[0]);
                 s[1] = mfma16_bf16(a, qf[1][ks], s[1]);
+                if constexpr (FP8 && ks + 1 < kK32) a_next = kfrag(kr[(ks + 1) % kLookK]);
                 if constexpr (!FP8 && ks == kK32 - 1) {
                     copy_col(std::integral_constant<int, 16>{}, nsrc, cur);
                     copy_col(std::integral_constant<int, 17>{}, nsrc, cur);
@@ -932,14 +937,18 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_hg_kernel(
             const auto r1 = __builtin_amdgcn_permlane16_swap(pk[0][1], pk[1][1], false, false);
             const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(r0[0], r1[0], r0[1], r1[1]));
 
-            // O^T += V^T P^T over the 16 dim tiles; V^T fragments kLookV ahead
+            // O^T += V^T P^T over the 16 dim tiles; V^T fragments kLookV ahead (FP8:
+            // expanded one MFMA ahead, as the K fragments above)
+            bf16x8 v_next;
+            if constexpr (FP8) v_next = vfrag(vr[0]);
             static_for<16>([&](auto dc) {
                 constexpr int dt = decltype(dc)::value;
-                const bf16x8 a = vfrag(vr[dt % kLookV]);
+                const bf16x8 a = FP8 ? v_next : vfrag(vr[dt % kLookV]);
                 if constexpr (dt + kLookV < 16) vr[dt % kLookV] = vload(dt + kLookV);
-                // wait states: pb (and, FP8, the converted V^T fragment) were just written by VALU code
+                // wait states: pb (and, FP8, the expanded V^T fragment) were written by VALU code
                 if constexpr (dt == 0 || FP8) asm volatile("s_nop 4");
                 mfma32_bf16_acc(o[dt], a, pb);                    // its operand reads of block dt are done
+                if constexpr (FP8 && dt + 1 < 16) v_next = vfrag(vr[(dt + 1) % kLookV]);
                 if constexpr (!FP8) copy_col(dc, nsrc, cur);
                 __builtin_amdgcn_sched_barrier(0);
             });
