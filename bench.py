@@ -11,9 +11,10 @@ each): cache stores -> indexer + top-k (the fused call) -> sparse MLA
 decode, in us/step, and the same step with the indexer and top-k as two calls.
 
 All inputs are seeded synthetic tensors generated on the GPU before timing.
-Each stage is bracketed by HIP events on the stream the kernels run on; the
-roofline object uses the algorithmic work per launch divided by the measured
-average launch time.  The CPU baseline runs the oracle (the plain
+The timed steps run without instrumentation; a second pass of the same steps
+brackets each stage by HIP events on the stream the kernels run on, and the
+roofline object uses the algorithmic work per launch divided by that average
+launch time.  The CPU baseline runs the oracle (the plain
 double-precision C reference) on a bounded sample of query rows of the same
 workload.
 
@@ -281,17 +282,24 @@ def decode_kernels(db, stages, mla_traffic_key="sparse_mla_decode"):
 
 
 def time_decode(args, cfg, inp, caches, newest, ds):
-    """Warm-up, then `args.steps` timed decode steps: (seconds per step, stage ms)."""
+    """Warm-up, then `args.steps` timed decode steps: (seconds per step, stage ms).
+    The timed steps carry no instrumentation (events between a step's launches
+    cost the GPU ≈ 20 us per step at this size); the stage times come from a
+    second pass of the same steps with events."""
     for _ in range(args.warmup):
         run_decode_step(cfg, inp, caches, newest, ds)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_decode_step(cfg, inp, caches, newest, ds)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
     timer = StageTimer(["store", "indexer_topk", "mla"] if ds.fused_ws is not None else
                        ["store", "indexer", "topk", "mla"])
-    t0 = time.perf_counter()
     for _ in range(args.steps):
         run_decode_step(cfg, inp, caches, newest, ds, timer)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / args.steps, timer.avg_ms()
+    return wall, timer.avg_ms()
 
 
 def time_decode_graph(args, cfg, inp, caches, newest, ds):
@@ -565,13 +573,18 @@ def main():
         run_prefill_step(cfg, inp, st, kv_slot)
     torch.cuda.synchronize()
     log(f"[bench] prefill warmup done; timing {args.steps} steps")
-    timer = StageTimer(["store", "indexer", "topk", "mla"])
+    # the timed steps carry no instrumentation; the stages come from a second
+    # pass of the same steps with events between the launches
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_prefill_step(cfg, inp, st, kv_slot, timer)
+        run_prefill_step(cfg, inp, st, kv_slot)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
+    timer = StageTimer(["store", "indexer", "topk", "mla"])
+    for _ in range(args.steps):
+        run_prefill_step(cfg, inp, st, kv_slot, timer)
+    torch.cuda.synchronize()
     stages = timer.avg_ms()
     ms_step = wall * 1e3
     tok_s = cfg.L / wall

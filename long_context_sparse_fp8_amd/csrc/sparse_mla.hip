@@ -388,14 +388,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                 lo = lds_tr16(p + v_off[0]);
                 hi = lds_tr16(p + v_off[1]);
             };
-            // softmax of the half just finished: p = 2^(c2 q.k - m_ref) (FP8: times
-            // the row scale in both places), packed to bf16 pairs of the P^T operand
+            // FP8 rows: softmax of the half just finished, p = 2^(logit - m_ref) with
+            // the logit c2 q.k times the row scale, and p times the row scale again
+            // (the scale of V), packed to bf16 pairs of the P^T operand
             auto softmax_half = [&](int hf) {
                 if (first_attempt && j == 0 && hf == 0) {   // reference of every head: max over rows 0..31
                     float mx = -INFINITY;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        float x = s[i] * (FP8 ? sm.f8logit[8 * (i >> 2) + 4 * g + (i & 3)] : c2);
+                        const float x = s[i] * sm.f8logit[8 * (i >> 2) + 4 * g + (i & 3)];
                         mx = fmaxf(mx, 8 * (i >> 2) + (i & 3) < lim ? x : -INFINITY);
                     }
                     m_ref = fmaxf(mx, swap_halves(mx));
@@ -409,20 +410,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
 #pragma unroll
                         for (int e = 0; e < 2; ++e) {
                             const int ii = i + e, rl = 32 * hf + 8 * (ii >> 2) + (ii & 3);
-                            float x, v = s[ii];
-                            if constexpr (FP8) {
-                                v *= sm.f8logit[rl + 4 * g];
-                                x = v - m_ref;
-                            } else {
-                                x = fmaf(v, c2, -m_ref);
-                            }
+                            float v = s[ii] * sm.f8logit[rl + 4 * g];
+                            float x = v - m_ref;
                             if constexpr (decltype(masked)::value) {
                                 if (!(rl < lim)) { x = -INFINITY; v = -INFINITY; }
                             }
                             rmax = fmaxf(rmax, v);
                             p[e] = __builtin_amdgcn_exp2f(x);
                             psum += p[e];
-                            if constexpr (FP8) p[e] *= sm.f8scale[rl + 4 * g];
+                            p[e] *= sm.f8scale[rl + 4 * g];
                         }
                         const bf16x2 pk = {(__bf16)p[0], (__bf16)p[1]};
                         pw[2 * hf + (i >> 3)][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
