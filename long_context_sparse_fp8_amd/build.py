@@ -50,6 +50,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # the library must load with every symbol resolved: hipcc can drop a kernel's
+    # host-side launch stub without an error (seen with an inline-asm operand of a
+    # 256-bit vector type), which would only show when the library is loaded
+    r = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r}).dsa_abi_version()"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{tmp} does not load:\n{r.stderr.strip()}")
     os.replace(tmp, LIB)
     return LIB
 
