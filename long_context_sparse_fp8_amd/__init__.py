@@ -8,7 +8,7 @@ of include/dsa.h (libdsa.so); this package is the Python binding of that
 ABI, with the same names.
 """
 from ._binding import (  # noqa: F401
-    DSAError, lib, abi_version, indexer_cache_store, kv_cache_store, indexer_scores, topk, topk_static,
+    DSAError, lib, abi_version, indexer_cache_store, kv_cache_store, cache_store, indexer_scores, topk, topk_static,
     topk_workspace_size, indexer_topk, indexer_topk_workspace_size,
     sparse_mla_prefill, sparse_mla_decode, sparse_mla_decode_workspace_size, LIB_PATH, PAGE, DK, DV,
     KV_BF16, KV_FP8_E4M3,

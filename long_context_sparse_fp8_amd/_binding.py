@@ -50,6 +50,8 @@ def lib():
     L.dsa_indexer_cache_store.argtypes = [P, P, P, i32, i32, P, P, i64, P]
     L.dsa_kv_cache_store.restype = ctypes.c_int
     L.dsa_kv_cache_store.argtypes = [P, P, i32, ctypes.c_int, P, P, i64, P]
+    L.dsa_cache_store.restype = ctypes.c_int
+    L.dsa_cache_store.argtypes = [P, P, P, i32, i32, P, P, i64, P, P, i32, ctypes.c_int, P, P, i64, P]
     L.dsa_indexer_scores.restype = ctypes.c_int
     L.dsa_indexer_scores.argtypes = [P, P, P, i64, P, P, i64, P, i64, P, P, i32, i32, i32, P, i64, P]
     L.dsa_topk_workspace_size.restype = sz
@@ -129,6 +131,29 @@ def kv_cache_store(kv_bf16, slot, kv_cache, kv_scale=None, stream=None):
                                     _ptr(kv_cache, torch.uint8 if fp8 else torch.bfloat16, "kv_cache"),
                                     _ptr(kv_scale, torch.float32, "kv_scale") if fp8 else None,
                                     kv_cache.shape[0], _stream(stream)))
+
+
+def cache_store(k_fp8, k_scale, key_slot, key_cache, key_scale_cache, kv_bf16, kv_slot, kv_cache, kv_scale=None,
+                stream=None):
+    """Both stores in one launch: indexer_cache_store(k_fp8, k_scale, key_slot, key_cache, key_scale_cache)
+    and kv_cache_store(kv_bf16, kv_slot, kv_cache, kv_scale), same arguments and results."""
+    n_keys, d_i = k_fp8.shape
+    n_pages = key_cache.shape[0]
+    assert key_cache.shape[1:] == (PAGE, d_i) and key_scale_cache.shape == (n_pages, PAGE)
+    n_kv = kv_bf16.shape[0]
+    assert kv_bf16.shape[1] == DK and kv_cache.shape[1] == DK
+    fp8 = kv_cache.dtype == torch.uint8
+    if fp8 and kv_scale is None:
+        raise ValueError("kv_scale is required for an FP8 cache")
+    _check(lib().dsa_cache_store(_ptr(k_fp8, torch.uint8, "k_fp8"), _ptr(k_scale, torch.float32, "k_scale"),
+                                 _ptr(key_slot, torch.int64, "key_slot"), n_keys, d_i,
+                                 _ptr(key_cache, torch.uint8, "key_cache"),
+                                 _ptr(key_scale_cache, torch.float32, "key_scale_cache"), n_pages,
+                                 _ptr(kv_bf16, torch.bfloat16, "kv_bf16"), _ptr(kv_slot, torch.int64, "kv_slot"), n_kv,
+                                 KV_FP8_E4M3 if fp8 else KV_BF16,
+                                 _ptr(kv_cache, torch.uint8 if fp8 else torch.bfloat16, "kv_cache"),
+                                 _ptr(kv_scale, torch.float32, "kv_scale") if fp8 else None,
+                                 kv_cache.shape[0], _stream(stream)))
 
 
 # ---------------------------------------------------------------- stage 1

@@ -12,17 +12,16 @@
 
 namespace dsa {
 
-// one thread per 16-byte chunk of a key
-__global__ void indexer_store_kernel(const uint8_t *__restrict__ k, const float *__restrict__ ks,
-                                     const int64_t *__restrict__ slot, int32_t n, int32_t d_i,
-                                     uint8_t *__restrict__ cache, float *__restrict__ scache,
-                                     int64_t n_slots) {
+// Thread `gid` of the key store: one 16-byte chunk of a key (d_i / 16 per key).
+__device__ __forceinline__ void indexer_store_chunk(int64_t gid, const uint8_t *__restrict__ k,
+                                                    const float *__restrict__ ks, const int64_t *__restrict__ slot,
+                                                    int32_t n, int32_t d_i, uint8_t *__restrict__ cache,
+                                                    float *__restrict__ scache, int64_t n_slots) {
     const int chunks = d_i / 16;
-    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t tok = gid / chunks;
-    int c = (int)(gid - tok * chunks);
+    const int64_t tok = gid / chunks;
+    const int c = (int)(gid - tok * chunks);
     if (tok >= n) return;
-    int64_t sl = slot[tok];
+    const int64_t sl = slot[tok];
     if (sl < 0 || sl >= n_slots) return;
     const uint4 v = reinterpret_cast<const uint4 *>(k + tok * d_i)[c];
     const int64_t page = sl / kPage;
@@ -31,29 +30,28 @@ __global__ void indexer_store_kernel(const uint8_t *__restrict__ k, const float 
     if (c == 0) scache[sl] = ks[tok];
 }
 
-// bf16 cache: one thread per 16-byte chunk (72 per row)
-__global__ void kv_store_bf16_kernel(const uint16_t *__restrict__ kv, const int64_t *__restrict__ slot,
-                                     int32_t n, uint16_t *__restrict__ cache, int64_t n_slots) {
+// Thread `gid` of the bf16 latent store: one 16-byte chunk of a row (72 per row).
+__device__ __forceinline__ void kv_store_bf16_chunk(int64_t gid, const uint16_t *__restrict__ kv,
+                                                    const int64_t *__restrict__ slot, int32_t n,
+                                                    uint16_t *__restrict__ cache, int64_t n_slots) {
     constexpr int kChunks = kDk * 2 / 16;
-    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t tok = gid / kChunks;
-    int c = (int)(gid - tok * kChunks);
+    const int64_t tok = gid / kChunks;
+    const int c = (int)(gid - tok * kChunks);
     if (tok >= n) return;
-    int64_t sl = slot[tok];
+    const int64_t sl = slot[tok];
     if (sl < 0 || sl >= n_slots) return;
     reinterpret_cast<uint4 *>(cache + sl * kDk)[c] = reinterpret_cast<const uint4 *>(kv + tok * kDk)[c];
 }
 
-// FP8 cache: one wave per token row; lane l owns elements l + 64 j, j < 9
-__global__ __launch_bounds__(256) void kv_store_fp8_kernel(const uint16_t *__restrict__ kv,
-                                                            const int64_t *__restrict__ slot, int32_t n,
-                                                            uint8_t *__restrict__ cache,
-                                                            float *__restrict__ scale_out, int64_t n_slots) {
+// FP8 latent store of token `tok` by one whole wave (tok is wave-uniform): lane
+// l owns elements l + 64 j, j < 9.
+__device__ __forceinline__ void kv_store_fp8_row(int64_t tok, int lane, const uint16_t *__restrict__ kv,
+                                                 const int64_t *__restrict__ slot, int32_t n,
+                                                 uint8_t *__restrict__ cache, float *__restrict__ scale_out,
+                                                 int64_t n_slots) {
     constexpr int kPer = kDk / kWave;  // 9
-    const int lane = threadIdx.x & 63;
-    int64_t tok = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
     if (tok >= n) return;
-    int64_t sl = slot[tok];
+    const int64_t sl = slot[tok];
     if (sl < 0 || sl >= n_slots) return;
     float x[kPer];
     float amax = 0.0f;
@@ -68,6 +66,51 @@ __global__ __launch_bounds__(256) void kv_store_fp8_kernel(const uint16_t *__res
     for (int j = 0; j < kPer; ++j)
         cache[sl * kDk + lane + kWave * j] = (uint8_t)f32_to_e4m3(__fdiv_rn(x[j], scale));
     if (lane == 0) scale_out[sl] = scale;
+}
+
+__global__ __launch_bounds__(256) void indexer_store_kernel(const uint8_t *__restrict__ k, const float *__restrict__ ks,
+                                                            const int64_t *__restrict__ slot, int32_t n, int32_t d_i,
+                                                            uint8_t *__restrict__ cache, float *__restrict__ scache,
+                                                            int64_t n_slots) {
+    indexer_store_chunk((int64_t)blockIdx.x * blockDim.x + threadIdx.x, k, ks, slot, n, d_i, cache, scache, n_slots);
+}
+
+__global__ __launch_bounds__(256) void kv_store_bf16_kernel(const uint16_t *__restrict__ kv,
+                                                            const int64_t *__restrict__ slot, int32_t n,
+                                                            uint16_t *__restrict__ cache, int64_t n_slots) {
+    kv_store_bf16_chunk((int64_t)blockIdx.x * blockDim.x + threadIdx.x, kv, slot, n, cache, n_slots);
+}
+
+// four tokens per 256-thread block
+__global__ __launch_bounds__(256) void kv_store_fp8_kernel(const uint16_t *__restrict__ kv,
+                                                            const int64_t *__restrict__ slot, int32_t n,
+                                                            uint8_t *__restrict__ cache,
+                                                            float *__restrict__ scale_out, int64_t n_slots) {
+    kv_store_fp8_row((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63, kv, slot, n, cache, scale_out,
+                     n_slots);
+}
+
+// Both stores in one launch: blocks [0, key_blocks) store keys, the rest latent
+// rows (the branch is uniform per block).  A step's new tokens are few, so each
+// store alone is a short launch whose fixed cost exceeds its work.
+template <bool FP8>
+__global__ __launch_bounds__(256) void cache_store_kernel(const uint8_t *__restrict__ k, const float *__restrict__ ks,
+                                                          const int64_t *__restrict__ key_slot, int32_t n_keys,
+                                                          int32_t d_i, uint8_t *__restrict__ key_cache,
+                                                          float *__restrict__ key_scache, int64_t n_key_slots,
+                                                          int64_t key_blocks, const uint16_t *__restrict__ kv,
+                                                          const int64_t *__restrict__ kv_slot, int32_t n_kv,
+                                                          void *__restrict__ kv_cache, float *__restrict__ kv_scale,
+                                                          int64_t n_slots) {
+    const int64_t b = blockIdx.x;
+    if (b < key_blocks) {
+        indexer_store_chunk(b * 256 + threadIdx.x, k, ks, key_slot, n_keys, d_i, key_cache, key_scache, n_key_slots);
+    } else if constexpr (FP8) {
+        kv_store_fp8_row((b - key_blocks) * 4 + (threadIdx.x >> 6), threadIdx.x & 63, kv, kv_slot, n_kv,
+                         (uint8_t *)kv_cache, kv_scale, n_slots);
+    } else {
+        kv_store_bf16_chunk((b - key_blocks) * 256 + threadIdx.x, kv, kv_slot, n_kv, (uint16_t *)kv_cache, n_slots);
+    }
 }
 
 hipError_t launch_indexer_store(const uint8_t *k, const float *ks, const int64_t *slot, int32_t n, int32_t d_i,
@@ -92,6 +135,24 @@ hipError_t launch_kv_store(const uint16_t *kv, const int64_t *slot, int32_t n, i
         hipLaunchKernelGGL(kv_store_fp8_kernel, dim3((unsigned)grid), dim3(256), 0, stream, kv, slot, n,
                            (uint8_t *)cache, scale, n_slots);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_store(const uint8_t *k, const float *ks, const int64_t *key_slot, int32_t n_keys, int32_t d_i,
+                              uint8_t *key_cache, float *key_scache, int64_t n_pages, const uint16_t *kv,
+                              const int64_t *kv_slot, int32_t n_kv, int dt, void *kv_cache, float *kv_scale,
+                              int64_t n_slots, hipStream_t stream) {
+    const int64_t key_blocks = ((int64_t)n_keys * (d_i / 16) + 255) / 256;
+    const int64_t kv_blocks = dt == 0 ? ((int64_t)n_kv * (kDk * 2 / 16) + 255) / 256 : ((int64_t)n_kv + 3) / 4;
+    const dim3 grid((unsigned)(key_blocks + kv_blocks));
+    if (dt == 0)
+        hipLaunchKernelGGL(cache_store_kernel<false>, grid, dim3(256), 0, stream, k, ks, key_slot, n_keys, d_i,
+                           key_cache, key_scache, n_pages * kPage, key_blocks, kv, kv_slot, n_kv, kv_cache, kv_scale,
+                           n_slots);
+    else
+        hipLaunchKernelGGL(cache_store_kernel<true>, grid, dim3(256), 0, stream, k, ks, key_slot, n_keys, d_i,
+                           key_cache, key_scache, n_pages * kPage, key_blocks, kv, kv_slot, n_kv, kv_cache, kv_scale,
+                           n_slots);
     return hipGetLastError();
 }
 

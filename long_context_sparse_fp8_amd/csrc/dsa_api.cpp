@@ -96,6 +96,38 @@ DSA_EXPORT dsa_status dsa_kv_cache_store(const uint16_t *kv_bf16, const int64_t 
     return DSA_OK;
 }
 
+DSA_EXPORT dsa_status dsa_cache_store(const uint8_t *k_fp8, const float *k_scale, const int64_t *key_slot,
+                                      int32_t n_keys, int32_t d_i, uint8_t *key_cache, float *key_scale_cache,
+                                      int64_t n_pages, const uint16_t *kv_bf16, const int64_t *kv_slot, int32_t n_kv,
+                                      dsa_kv_dtype dt, void *kv_cache, float *kv_scale, int64_t n_slots,
+                                      void *stream) {
+    REQUIRE(n_keys >= 0 && n_kv >= 0, DSA_ERR_BAD_SHAPE, "dsa_cache_store: n_keys = %d, n_kv = %d (need >= 0)", n_keys,
+            n_kv);
+    REQUIRE(n_pages >= 0, DSA_ERR_BAD_SHAPE, "dsa_cache_store: n_pages = %lld < 0", (long long)n_pages);
+    REQUIRE(n_slots >= 0, DSA_ERR_BAD_SHAPE, "dsa_cache_store: n_slots < 0");
+    REQUIRE(d_i == 64 || d_i == 128, DSA_ERR_UNSUPPORTED, "dsa_cache_store: d_i = %d not in {64, 128}", d_i);
+    REQUIRE(dt == DSA_KV_BF16 || dt == DSA_KV_FP8_E4M3, DSA_ERR_UNSUPPORTED, "dsa_cache_store: bad dtype %d", (int)dt);
+    if (n_keys == 0 && n_kv == 0) return DSA_OK;
+    if (n_keys > 0) {
+        REQUIRE_PTR(k_fp8);
+        REQUIRE_PTR(k_scale);
+        REQUIRE_PTR(key_slot);
+        REQUIRE_PTR(key_cache);
+        REQUIRE_PTR(key_scale_cache);
+    }
+    if (n_kv > 0) {
+        REQUIRE_PTR(kv_bf16);
+        REQUIRE_PTR(kv_slot);
+        REQUIRE_PTR(kv_cache);
+        if (dt == DSA_KV_FP8_E4M3) REQUIRE_PTR(kv_scale);
+    }
+    hipError_t e = dsa::launch_cache_store(k_fp8, k_scale, key_slot, n_keys, d_i, key_cache, key_scale_cache, n_pages,
+                                           kv_bf16, kv_slot, n_kv, (int)dt, kv_cache, kv_scale, n_slots,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "dsa_cache_store launch");
+    return DSA_OK;
+}
+
 DSA_EXPORT dsa_status dsa_indexer_scores(const uint8_t *q_fp8, const float *q_scale, const float *w, int64_t w_ld,
                                          const uint8_t *key_cache, const float *key_scale_cache, int64_t n_pages,
                                          const int32_t *page_table, int64_t pt_ld, const int32_t *q_seq,

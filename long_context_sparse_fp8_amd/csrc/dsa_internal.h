@@ -81,6 +81,11 @@ hipError_t launch_indexer_store(const uint8_t *k, const float *ks, const int64_t
                                 uint8_t *cache, float *scache, int64_t n_pages, hipStream_t stream);
 hipError_t launch_kv_store(const uint16_t *kv, const int64_t *slot, int32_t n, int dt, void *cache, float *scale,
                            int64_t n_slots, hipStream_t stream);
+// both stores in one launch (n_keys or n_kv may be 0)
+hipError_t launch_cache_store(const uint8_t *k, const float *ks, const int64_t *key_slot, int32_t n_keys, int32_t d_i,
+                              uint8_t *key_cache, float *key_scache, int64_t n_pages, const uint16_t *kv,
+                              const int64_t *kv_slot, int32_t n_kv, int dt, void *kv_cache, float *kv_scale,
+                              int64_t n_slots, hipStream_t stream);
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream);
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *q_pos, int32_t n_q, int32_t k, int32_t *idx,
                        void *ws, size_t ws_bytes, hipStream_t stream);

@@ -42,9 +42,8 @@ def alloc_prefill(n_pages, d_i, n_slots, rows, ld, k, h, kv_fp8=False, with_lse=
 
 
 def store_tokens(st: PrefillState, ik, ik_scale, ik_slot, kv, kv_slot):
-    """Write new tokens' indexer keys and latent rows into the two caches."""
-    B.indexer_cache_store(ik, ik_scale, ik_slot, st.key_cache, st.key_scale)
-    B.kv_cache_store(kv, kv_slot, st.kv_cache, st.kv_scale)
+    """Write new tokens' indexer keys and latent rows into the two caches (one launch)."""
+    B.cache_store(ik, ik_scale, ik_slot, st.key_cache, st.key_scale, kv, kv_slot, st.kv_cache, st.kv_scale)
 
 
 def prefill_step(st: PrefillState, iq, iq_scale, w, page_table, kv_slot_table, q_seq, q_pos, q, k, sm_scale,

@@ -155,6 +155,24 @@ def test_cache_store_validation(L):
     assert L.dsa_kv_cache_store(A, MIS, 10, 0, A, None, 100, None) == 4
 
 
+def test_combined_cache_store_validation(L):
+    """dsa_cache_store applies the checks of both stores, before anything is
+    enqueued; a zero count makes that side's pointers optional."""
+    st = L.dsa_cache_store
+    # (k, k_scale, key_slot, n_keys, d_i, key_cache, key_scale, n_pages,
+    #  kv, kv_slot, n_kv, dt, kv_cache, kv_scale, n_slots, stream)
+    assert st(None, None, None, 0, 128, None, None, 4, None, None, 0, 0, None, None, 10, None) == 0
+    assert st(None, None, None, 0, 96, None, None, 4, None, None, 0, 0, None, None, 10, None) == 3     # d_i
+    assert st(None, None, None, 0, 128, None, None, 4, None, None, 0, 5, None, None, 10, None) == 3    # dtype
+    assert st(A, A, A, -1, 128, A, A, 4, A, A, 1, 0, A, None, 10, None) == 2
+    assert st(A, A, A, 1, 128, A, A, 4, A, A, -1, 0, A, None, 10, None) == 2
+    assert st(A, A, A, 1, 128, A, A, -1, None, None, 0, 0, None, None, 10, None) == 2               # n_pages
+    assert st(None, A, A, 10, 128, A, A, 4, None, None, 0, 0, None, None, 10, None) == 1             # keys stored
+    assert st(A, A, A, 10, 128, A, None, 4, None, None, 0, 0, None, None, 10, None) == 1
+    assert st(None, None, None, 0, 128, None, None, 4, A, A, 10, 1, A, None, 10, None) == 1          # FP8: kv_scale
+    assert st(None, None, None, 0, 128, None, None, 4, A, MIS, 10, 0, A, None, 10, None) == 4        # misaligned
+
+
 def test_zero_counts_enqueue_nothing(L):
     """n = 0 / n_q = 0: OK with NULL data pointers (no device needed), while the
     shape and support checks still apply."""

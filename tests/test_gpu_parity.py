@@ -125,6 +125,52 @@ def test_cache_store_fp8_matches_oracle_quantizer():
     assert scale.cpu().numpy()[np.setdiff1d(np.arange(n_slots), s[ok])].max() == -1.0
 
 
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_cache_store_one_launch_equals_the_two_stores(kv_fp8):
+    """dsa_cache_store writes the bytes the two separate stores write (different
+    key and row counts, slots past either cache and negative slots skipped), a
+    zero count leaves that cache untouched, and both zero change nothing."""
+    say(f"[cache_store] one launch, fp8={kv_fp8}")
+    n_keys, n_kv, n_pages, d_i, n_slots = 70, 45, 2, 128, 90
+    g = synth.gen(4343)
+    ik = torch.randint(0, 256, (n_keys, d_i), generator=g, dtype=torch.int64).to(torch.uint8)
+    iks = torch.rand(n_keys, generator=g) + 0.5
+    key_slot = synth.randperm(n_pages * 64 + 12, 4344)[:n_keys].long()     # some past the key cache
+    key_slot[3] = -1
+    kv = synth.bf16_normal((n_kv, 576), 4345)
+    kv_slot = synth.randperm(n_slots + 6, 4346)[:n_kv].long()               # some past the latent cache
+    kv_slot[4] = -1
+    d = lambda x: x.to(DEV)
+
+    def fresh():
+        kc = torch.full((n_pages, 64, d_i), 0x11, dtype=torch.uint8, device=DEV)
+        ks = torch.full((n_pages, 64), -3.0, device=DEV)
+        if kv_fp8:
+            return [kc, ks, torch.full((n_slots, 576), 0x22, dtype=torch.uint8, device=DEV),
+                    torch.full((n_slots,), -1.0, device=DEV)]
+        return [kc, ks, torch.full((n_slots, 576), 0x1234, dtype=torch.int16, device=DEV).view(torch.bfloat16), None]
+
+    raw = lambda t: t.cpu().contiguous().view(torch.uint8)
+    two, one, keys_only, rows_only, none, untouched = (fresh() for _ in range(6))
+    dsa.indexer_cache_store(d(ik), d(iks), d(key_slot), two[0], two[1])
+    dsa.kv_cache_store(d(kv), d(kv_slot), two[2], two[3])
+    dsa.cache_store(d(ik), d(iks), d(key_slot), one[0], one[1], d(kv), d(kv_slot), one[2], one[3])
+    dsa.cache_store(d(ik), d(iks), d(key_slot), keys_only[0], keys_only[1], d(kv[:0]), d(kv_slot[:0]),
+                    keys_only[2], keys_only[3])
+    dsa.cache_store(d(ik[:0]), d(iks[:0]), d(key_slot[:0]), rows_only[0], rows_only[1], d(kv), d(kv_slot),
+                    rows_only[2], rows_only[3])
+    dsa.cache_store(d(ik[:0]), d(iks[:0]), d(key_slot[:0]), none[0], none[1], d(kv[:0]), d(kv_slot[:0]),
+                    none[2], none[3])
+    torch.cuda.synchronize()
+    n_parts = 4 if kv_fp8 else 3
+    for i in range(n_parts):
+        assert torch.equal(raw(one[i]), raw(two[i])), i
+        assert torch.equal(raw(none[i]), raw(untouched[i])), i
+        assert torch.equal(raw(keys_only[i]), raw(two[i] if i < 2 else untouched[i])), i
+        assert torch.equal(raw(rows_only[i]), raw(untouched[i] if i < 2 else two[i])), i
+    assert not torch.equal(raw(two[0]), raw(untouched[0])) and not torch.equal(raw(two[2]), raw(untouched[2]))
+
+
 # ------------------------------------------------------------------ indexer
 def _oracle_scores(inp, rows, ld):
     return oracle.indexer_scores(u8(inp.iq[rows]), inp.iq_scale[rows].numpy(), inp.w[rows].numpy(), u8(inp.ik),
