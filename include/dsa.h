@@ -120,13 +120,16 @@ dsa_status dsa_indexer_cache_store(const uint8_t *k_fp8, const float *k_scale, c
 dsa_status dsa_kv_cache_store(const uint16_t *kv_bf16, const int64_t *slot, int32_t n, dsa_kv_dtype dt,
                               void *kv_cache, float *kv_scale, int64_t n_slots, void *stream);
 
-/* Both stores above in one launch: the indexer keys of n_keys tokens (as
- * dsa_indexer_cache_store) and the latent rows of n_kv tokens (as
- * dsa_kv_cache_store), with the same arguments, layouts and skipped slots;
- * the bytes written are the same as those of the two calls.  A decode step
- * stores a handful of tokens, for which each store alone is a short launch
- * whose fixed cost exceeds its work.  n_keys == 0 or n_kv == 0 leaves that
- * cache alone (its pointers may then be NULL); both zero enqueues nothing. */
+/* Both stores above in one launch, writing new tokens into the two caches of
+ * the announcement's "DeepSeek Sparse Attention" section: the indexer keys of
+ * n_keys tokens (as dsa_indexer_cache_store) and the latent rows of n_kv
+ * tokens (as dsa_kv_cache_store), with the same arguments, layouts and
+ * skipped slots; the bytes written are the same as those of the two calls.
+ * A decode step stores a handful of tokens, for which each store alone is a
+ * short launch whose fixed cost exceeds its work.  n_keys == 0 or n_kv == 0
+ * leaves that cache alone (its pointers may then be NULL); both zero
+ * enqueues nothing.  Argument errors are those of the two calls, reported
+ * before anything is enqueued. */
 dsa_status dsa_cache_store(const uint8_t *k_fp8, const float *k_scale, const int64_t *key_slot, int32_t n_keys,
                            int32_t d_i, uint8_t *key_cache, float *key_scale_cache, int64_t n_pages,
                            const uint16_t *kv_bf16, const int64_t *kv_slot, int32_t n_kv, dsa_kv_dtype dt,
