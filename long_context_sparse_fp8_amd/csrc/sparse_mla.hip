@@ -190,9 +190,16 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
     const int i16 = lane & 15, hd = (lane >> 4) & 1;
     // decode: workgroup b takes query b % n_q, split b / n_q, so that the splits of
     // a query are n_q apart in launch order and (with workgroups dealt round-robin
-    // to the 8 XCDs, n_q a multiple of 8) share one XCD's L2 for q and the indices
+    // to the 8 XCDs, n_q a multiple of 8) share one XCD's L2 for q and the indices.
+    // prefill: the last query first.  Later rows of a causal prefill select from
+    // longer prefixes, all but the first k rows the same number of entries, so
+    // the workgroups that start together end together and the next ones again
+    // start together; each walks its selection in ascending position, so the
+    // queries an XCD runs at once gather from the same stretch of the cache at
+    // the same time (more L2 hits than when the short first rows start the
+    // launch and scatter the phases).
     const int n_q_split = SPLIT ? (int)gridDim.x / n_splits : 0;
-    const int t = SPLIT ? (int)blockIdx.x % n_q_split : (int)blockIdx.x;
+    const int t = SPLIT ? (int)blockIdx.x % n_q_split : (int)(gridDim.x - 1 - blockIdx.x);
     const int split = SPLIT ? (int)blockIdx.x / n_q_split : 0;
     const int per_split = SPLIT ? (k + n_splits - 1) / n_splits : k;
     const int i_begin = split * per_split;
