@@ -26,8 +26,9 @@
 //     half 1 and that of half 1 over the O^T MFMAs of rows 0..31, a few VALU
 //     instructions per MFMA in a three-stage software pipeline (a wave issues
 //     independent VALU work while its own MFMA executes, but in order, so no
-//     instruction may wait on another of the same slot).  FP8 rows keep each
-//     half's softmax between the MFMAs;
+//     instruction may wait on another of the same slot).  FP8 rows keep half
+//     0's softmax between the MFMAs (one accumulator), half 1's runs under the
+//     O^T MFMAs of rows 0..31 likewise;
 //   * softmax per head (= per lane column) in the exp2 domain against a fixed
 //     reference: the head's maximum over the first 32 rows.  Probabilities of
 //     later rows may exceed 1 by up to 2^64 before the reference must move; that
@@ -434,8 +435,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                 if (partial) body(std::true_type{});
                 else body(std::false_type{});
             };
-            // The MFMA stream of one tile.  SERIAL (FP8 rows): each half's softmax
-            // runs between the MFMAs of S^T and O^T.  bf16 rows: the softmax is spread
+            // The MFMA stream of one tile.  SERIAL (FP8 rows): half 0's softmax runs
+            // between the S^T MFMAs of the two halves (one accumulator), half 1's is
+            // spread over the O^T MFMAs of rows 0..31.  bf16 rows: the softmax is spread
             // over the following MFMAs, about one element per MFMA (an exp2 and five
             // other VALU instructions, which the wave issues while its MFMA executes):
             // half 0's under the S^T MFMAs of half 1 (a second accumulator), half 1's
@@ -480,6 +482,33 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                         xs[t % 3] = fmaf(v, c2, -m_ref);
                     }
                 };
+                float lg1[16], sc1[16];               // FP8: half 1's row scales of this lane
+                auto f8_slot = [&](auto tc, const f32x16 &sv) {
+                    constexpr int t = decltype(tc)::value;
+                    if constexpr (t >= 2 && t < 18) {
+                        constexpr int e = t - 2;
+                        float p = keep[e % 3] ? pes[e % 3] : 0.0f;
+                        psum += p;
+                        asm volatile("" : "+v"(psum));
+                        p *= sc1[e];
+                        if constexpr (e & 1) {
+                            const bf16x2 pk = {(__bf16)pprev, (__bf16)p};
+                            pw[2 + (e >> 3)][(e & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+                        } else {
+                            pprev = p;
+                        }
+                    }
+                    if constexpr (t >= 1 && t < 17) {
+                        constexpr int e = t - 1;
+                        pes[e % 3] = __builtin_amdgcn_exp2f(xs[e % 3]);
+                        keep[e % 3] = 32 + 8 * (e >> 2) + (e & 3) < lim;
+                    }
+                    if constexpr (t < 16) {
+                        const float v = sv[t] * lg1[t];
+                        rmax = fmaxf(rmax, v);
+                        xs[t % 3] = v - m_ref;
+                    }
+                };
 #pragma unroll
                 for (int f = 0; f < kLookK<FP8>; ++f) kr[f] = kload(f);
                 static_for<kQK>([&](auto fc) {
@@ -509,7 +538,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                         sm_slot(std::integral_constant<int, 0>{}, std::integral_constant<int, f - kKSteps - 2>{}, s);
                     __builtin_amdgcn_sched_barrier(0);
                 });
-                if constexpr (kSerial) softmax_half(1);
+                if constexpr (kSerial) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float4 a = *reinterpret_cast<const float4 *>(&sm.f8logit[32 + 8 * jj + 4 * g]);
+                        const float4 b = *reinterpret_cast<const float4 *>(&sm.f8scale[32 + 8 * jj + 4 * g]);
+                        lg1[4 * jj] = a.x; lg1[4 * jj + 1] = a.y; lg1[4 * jj + 2] = a.z; lg1[4 * jj + 3] = a.w;
+                        sc1[4 * jj] = b.x; sc1[4 * jj + 1] = b.y; sc1[4 * jj + 2] = b.z; sc1[4 * jj + 3] = b.w;
+                    }
+                }
                 static_for<kPV>([&](auto fc) {
                     constexpr int f = decltype(fc)::value;
                     if constexpr ((f + kQK) % kCopyEvery == 0 && (f + kQK) / kCopyEvery < kCopies)
@@ -520,10 +557,11 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_mla_kernel(
                     const uint4 bw = make_uint4(pw[f >> 4][0], pw[f >> 4][1], pw[f >> 4][2], pw[f >> 4][3]);
                     // wait states: P^T was just written by VALU code (serial: before the
                     // first O^T MFMA; overlapped: half 1's before the first MFMA of rows 32..63)
-                    if constexpr (kSerial ? f == 0 : f == kPV / 2) asm volatile("s_nop 4");
+                    if constexpr (f == kPV / 2) asm volatile("s_nop 4");
                     mfma32_bf16_acc(o[f & 15], a, __builtin_bit_cast(bf16x8, bw));
                     if constexpr (!kSerial && f >= 2 && f < 20)
                         sm_slot(std::integral_constant<int, 1>{}, std::integral_constant<int, f - 2>{}, s1);
+                    if constexpr (kSerial && f >= 2 && f < 20) f8_slot(std::integral_constant<int, f - 2>{}, s);
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
