@@ -7,8 +7,8 @@
 // degeneration of the deployment article, section 5.1).
 //
 // One workgroup per row: 512 threads when many rows of at most 32K scores are
-// selected at once (two workgroups share a CU, so one row's barriers and loads
-// overlap the other's work), else 1024.  Every score is touched by only two
+// selected at once (three workgroups share a CU, so one row's barriers and
+// loads overlap the others' work), else 1024.  Every score is touched by only two
 // cheap sweeps:
 //   1. an 11-bit histogram of the top key bits (sign, exponent, two mantissa
 //      bits) in LDS, NT / 128 lane-interleaved copies; a block scan of the 2048
@@ -55,7 +55,7 @@ constexpr int kCopies = 4;                      // lane-interleaved copies of th
 constexpr int kStreamAhead = 8;                 // chunks in flight per thread when a row is streamed
 
 // Workgroup shape: NT threads (1024, or 512 for rows of at most 32K scores,
-// two workgroups per CU), chunks of 4 NT scores; C > 0 chunks per row in
+// three workgroups per CU), chunks of 4 NT scores; C > 0 chunks per row in
 // registers, C == 0 streamed.
 template <int NT, int C>
 struct TopkShape {
@@ -201,8 +201,13 @@ __device__ __forceinline__ int topk_row_parts(int n, int k, int parts) {
 // otherwise the part's k survivors (original index and score) go to the
 // workspace at [t, part].  kMerge: the survivors of row t (rows of one part are
 // done already).
+// Waves per SIMD (launch bound): 6 for the register forms of 512 threads, i.e.
+// three workgroups per CU, which their LDS (at most 53 KB) allows; the rows of
+// up to 32K scores then keep 80 registers and park two chunks of keys in
+// scratch, and still run 19% faster than two workgroups per CU (0.95 against
+// 1.19 ms for the 32K prefill): the selection waits on barriers and loads.
 template <int NT, int C, bool VEC, int MODE>
-__global__ __launch_bounds__(NT, 1024 / NT) void topk_kernel(const float *__restrict__ scores, int64_t ld,
+__global__ __launch_bounds__(NT, NT == 512 && C > 0 ? 6 : 1024 / NT) void topk_kernel(const float *__restrict__ scores, int64_t ld,
                                                              const int32_t *__restrict__ q_pos, int32_t k,
                                                              int32_t *__restrict__ idx, int32_t parts,
                                                              float *__restrict__ ws_score,
@@ -862,9 +867,10 @@ static void launch_rows(dim3 grid, int64_t len, bool vec, const float *scores, i
     hipLaunchKernelGGL((topk_kernel<NT, C, V, MODE>), grid, dim3(NT), 0, stream, scores, ld, q_pos, k, idx, parts,    \
                        ws_score, ws_idx)
     if constexpr (MODE != kMerge) {
-        // more rows (or parts) than a 256-CU device has CUs: two workgroups of 512
-        // per CU while a row fits their registers (128 decode rows in 4 parts:
-        // 58 -> 51 us); with fewer, one workgroup of 1024 per row
+        // more rows (or parts) than a 256-CU device has CUs: workgroups of 512,
+        // three per CU, while a row fits their registers (128 decode rows in 4
+        // parts, then two per CU: 58 -> 51 us); with fewer, one workgroup of 1024
+        // per row
         if (len <= 16 * 2048 && (int64_t)grid.x * grid.y > 256) {
             if (vec) {
                 if (len <= 8 * 2048) DSA_TOPK_GO(512, 8, true);
